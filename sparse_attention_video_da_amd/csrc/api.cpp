@@ -1,0 +1,276 @@
+// C ABI of the decoupled sparse attention library: argument validation, plan compilation
+// (mask -> per-query-block exact lists, device workspace) and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/decoupattn.h"
+#include "da_internal.h"
+
+namespace da {
+hipError_t prepare_forward_kernels();
+hipError_t prepare_reassign_kernels();
+}  // namespace da
+
+struct da_plan_s {
+  da_desc desc;
+  int32_t nb;
+  float scale;
+  std::vector<int32_t> rowptr;  // [mask_heads][nb + 1], absolute offsets into col
+  std::vector<int32_t> col;
+  int32_t* d_rowptr = nullptr;
+  int32_t* d_col = nullptr;
+  int32_t* d_hist = nullptr;
+  int32_t* d_off = nullptr;
+  int32_t* d_start = nullptr;
+  int32_t* d_perm = nullptr;
+  int64_t bytes = 0;
+  int device = 0;
+};
+
+namespace {
+
+constexpr int32_t kMaxClusters = 8192;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(const da_desc& d) { return d.dtype == DA_DTYPE_BF16 ? 2 : 4; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+da_status check_desc(const da_desc* d) {
+  if (d == nullptr) return DA_ERR_INVALID_ARGUMENT;
+  if (d->heads < 1 || d->seq_len < 1 || d->clusters < 1 || d->head_dim < 1 || d->block < 1)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (d->clusters > d->seq_len) return DA_ERR_INVALID_ARGUMENT;
+  if (d->mask_heads != 1 && d->mask_heads != d->heads) return DA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(d->scale) || d->scale < 0.f) return DA_ERR_INVALID_ARGUMENT;
+  if (d->dtype != DA_DTYPE_F32 && d->dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return DA_ERR_UNSUPPORTED;
+  if (d->block != 64 && d->block != 128) return DA_ERR_UNSUPPORTED;
+  if (d->clusters > kMaxClusters) return DA_ERR_UNSUPPORTED;
+  // int32 indexing of [H][N][d] element offsets and [H][nb][C] counts
+  const int64_t nb = (d->seq_len + d->block - 1) / d->block;
+  if ((int64_t)d->seq_len * d->head_dim > INT32_MAX || nb * d->clusters > INT32_MAX ||
+      nb * nb * d->mask_heads > INT32_MAX)
+    return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+void destroy_device(da_plan_s* p) {
+  int32_t* bufs[] = {p->d_rowptr, p->d_col, p->d_hist, p->d_off, p->d_start, p->d_perm};
+  for (int32_t* b : bufs)
+    if (b) (void)hipFree(b);
+  p->d_rowptr = p->d_col = p->d_hist = p->d_off = p->d_start = p->d_perm = nullptr;
+}
+
+std::once_flag g_prep_once;
+hipError_t g_prep_err = hipSuccess;
+
+}  // namespace
+
+extern "C" {
+
+DA_API const char* da_status_str(da_status s) {
+  switch (s) {
+    case DA_OK: return "DA_OK";
+    case DA_ERR_INVALID_ARGUMENT: return "DA_ERR_INVALID_ARGUMENT: invalid argument";
+    case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED: unsupported size or dtype";
+    case DA_ERR_OUT_OF_MEMORY: return "DA_ERR_OUT_OF_MEMORY: device allocation failed";
+    case DA_ERR_DEVICE: return "DA_ERR_DEVICE: HIP device or launch error";
+  }
+  return "unknown status";
+}
+
+DA_API int32_t da_version(void) { return 100; }
+
+DA_API da_status da_validate_desc(const da_desc* desc, const uint8_t* mask) {
+  const da_status st = check_desc(desc);
+  if (st != DA_OK) return st;
+  if (mask == nullptr) return DA_ERR_INVALID_ARGUMENT;
+  return DA_OK;
+}
+
+DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_plan* out) {
+  if (out == nullptr) return DA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const da_status st = da_validate_desc(desc, mask);
+  if (st != DA_OK) return st;
+
+  da_plan_s* p = new (std::nothrow) da_plan_s();
+  if (p == nullptr) return DA_ERR_OUT_OF_MEMORY;
+  p->desc = *desc;
+  const int32_t nb = (desc->seq_len + desc->block - 1) / desc->block;
+  p->nb = nb;
+  p->scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt((float)desc->head_dim);
+  // Exact lists: for each mask head and query block, the ascending key blocks kept exact.
+  p->rowptr.resize((size_t)desc->mask_heads * (nb + 1));
+  for (int32_t mh = 0; mh < desc->mask_heads; ++mh) {
+    const uint8_t* m = mask + (size_t)mh * nb * nb;
+    for (int32_t b = 0; b < nb; ++b) {
+      p->rowptr[(size_t)mh * (nb + 1) + b] = (int32_t)p->col.size();
+      for (int32_t kb = 0; kb < nb; ++kb)
+        if (m[(size_t)b * nb + kb]) p->col.push_back(kb);
+    }
+    p->rowptr[(size_t)mh * (nb + 1) + nb] = (int32_t)p->col.size();
+  }
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1 || hipGetDevice(&p->device) != hipSuccess) {
+    delete p;
+    return DA_ERR_DEVICE;
+  }
+  std::call_once(g_prep_once, [] {
+    g_prep_err = da::prepare_forward_kernels();
+    if (g_prep_err == hipSuccess) g_prep_err = da::prepare_reassign_kernels();
+  });
+  if (g_prep_err != hipSuccess) {
+    delete p;
+    return DA_ERR_DEVICE;
+  }
+
+  const size_t H = desc->heads, N = desc->seq_len, C = desc->clusters;
+  const size_t n_rowptr = p->rowptr.size(), n_col = std::max<size_t>(1, p->col.size());
+  struct Alloc { int32_t** ptr; size_t n; } allocs[] = {
+      {&p->d_rowptr, n_rowptr}, {&p->d_col, n_col},        {&p->d_hist, H * nb * C},
+      {&p->d_off, H * nb * C},  {&p->d_start, H * C},      {&p->d_perm, H * N}};
+  for (const Alloc& a : allocs) {
+    if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      destroy_device(p);
+      delete p;
+      return DA_ERR_OUT_OF_MEMORY;
+    }
+    p->bytes += (int64_t)(a.n * sizeof(int32_t));
+  }
+  if (hipMemcpy(p->d_rowptr, p->rowptr.data(), n_rowptr * sizeof(int32_t),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      (!p->col.empty() && hipMemcpy(p->d_col, p->col.data(), p->col.size() * sizeof(int32_t),
+                                    hipMemcpyHostToDevice) != hipSuccess)) {
+    destroy_device(p);
+    delete p;
+    return DA_ERR_DEVICE;
+  }
+  *out = p;
+  return DA_OK;
+}
+
+DA_API da_status da_plan_destroy(da_plan p) {
+  if (p == nullptr) return DA_OK;
+  (void)hipDeviceSynchronize();
+  destroy_device(p);
+  delete p;
+  return DA_OK;
+}
+
+DA_API da_status da_plan_info(da_plan p, int32_t* num_blocks, int64_t* exact_pairs,
+                              int64_t* workspace_bytes) {
+  if (p == nullptr) return DA_ERR_INVALID_ARGUMENT;
+  if (num_blocks) *num_blocks = p->nb;
+  if (exact_pairs) *exact_pairs = (int64_t)p->col.size();
+  if (workspace_bytes) *workspace_bytes = p->bytes;
+  return DA_OK;
+}
+
+DA_API da_status da_plan_exact_lists(da_plan p, int32_t mh, int32_t* rowptr, int32_t* col) {
+  if (p == nullptr || mh < 0 || mh >= p->desc.mask_heads) return DA_ERR_INVALID_ARGUMENT;
+  const size_t base = (size_t)mh * (p->nb + 1);
+  const int32_t first = p->rowptr[base];
+  if (rowptr)
+    for (int32_t b = 0; b <= p->nb; ++b) rowptr[b] = p->rowptr[base + b] - first;
+  if (col)
+    for (int32_t i = first; i < p->rowptr[base + p->nb]; ++i) col[i - first] = p->col[i];
+  return DA_OK;
+}
+
+DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void* centroids_in,
+                             void* centroids_out, void* mean_values_out, int32_t* assign_out,
+                             int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                             void* stream) {
+  if (p == nullptr || K == nullptr || V == nullptr || centroids_in == nullptr ||
+      centroids_out == nullptr || mean_values_out == nullptr || assign_out == nullptr ||
+      cluster_sizes_out == nullptr || qblock_counts_out == nullptr)
+    return DA_ERR_INVALID_ARGUMENT;
+  const da_desc& d = p->desc;
+  const size_t es = elem_size(d);
+  const size_t cache_bytes = (size_t)d.heads * d.clusters * d.head_dim * es;
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(centroids_in, 16) ||
+      !aligned(centroids_out, 16) || !aligned(mean_values_out, 16) || !aligned(assign_out, 4) ||
+      !aligned(cluster_sizes_out, 4) || !aligned(qblock_counts_out, 4))
+    return DA_ERR_INVALID_ARGUMENT;
+  const size_t H = d.heads, N = d.seq_len, C = d.clusters;
+  const void* outs[] = {centroids_out, mean_values_out, assign_out, cluster_sizes_out,
+                        qblock_counts_out};
+  const size_t out_bytes[] = {cache_bytes, cache_bytes, H * N * 4, H * C * 4,
+                              H * (size_t)p->nb * C * 4};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(centroids_in, cache_bytes, outs[i], out_bytes[i])) return DA_ERR_INVALID_ARGUMENT;
+  da::ReassignArgs a{};
+  a.K = K;
+  a.V = V;
+  a.mu_in = centroids_in;
+  a.mu_out = centroids_out;
+  a.vbar_out = mean_values_out;
+  a.assign = assign_out;
+  a.sizes = cluster_sizes_out;
+  a.counts = qblock_counts_out;
+  a.rowptr = p->d_rowptr;
+  a.col = p->d_col;
+  a.hist = p->d_hist;
+  a.off = p->d_off;
+  a.start = p->d_start;
+  a.perm = p->d_perm;
+  a.H = d.heads;
+  a.N = d.seq_len;
+  a.C = d.clusters;
+  a.nb = p->nb;
+  a.block = d.block;
+  a.mask_heads = d.mask_heads;
+  const hipError_t e = da::launch_reassign(a, d.head_dim, d.dtype == DA_DTYPE_BF16,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;
+}
+
+DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void* V,
+                            const void* centroids, const void* mean_values,
+                            const int32_t* qblock_counts, void* O, float* lse_out,
+                            void* stream) {
+  if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || centroids == nullptr ||
+      mean_values == nullptr || qblock_counts == nullptr || O == nullptr)
+    return DA_ERR_INVALID_ARGUMENT;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(centroids, 16) ||
+      !aligned(mean_values, 16) || !aligned(O, 16) || !aligned(qblock_counts, 4) ||
+      (lse_out != nullptr && !aligned(lse_out, 4)))
+    return DA_ERR_INVALID_ARGUMENT;
+  const da_desc& d = p->desc;
+  da::FwdArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.mu = centroids;
+  a.vbar = mean_values;
+  a.counts = qblock_counts;
+  a.rowptr = p->d_rowptr;
+  a.col = p->d_col;
+  a.O = O;
+  a.lse = lse_out;
+  a.H = d.heads;
+  a.N = d.seq_len;
+  a.C = d.clusters;
+  a.nb = p->nb;
+  a.mask_heads = d.mask_heads;
+  a.scale_log2e = p->scale * 1.4426950408889634f;
+  const hipError_t e = da::launch_forward(a, d.head_dim, d.block, d.dtype == DA_DTYPE_BF16,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+// Everything the fused forward kernel reads, in device memory.
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* mu;        // [H][C][d] centroid keys
+  const void* vbar;      // [H][C][d] mean values
+  const int32_t* counts; // [H][nb][C]
+  const int32_t* rowptr; // [mask_heads][nb + 1], absolute offsets into col
+  const int32_t* col;    // sorted exact key blocks
+  void* O;
+  float* lse;            // may be null
+  int H, N, C, nb, mask_heads;
+  float scale_log2e;     // softmax scale * log2(e)
+};
+
+struct ReassignArgs {
+  const void* K;
+  const void* V;
+  const void* mu_in;
+  void* mu_out;
+  void* vbar_out;
+  int32_t* assign;
+  int32_t* sizes;
+  int32_t* counts;
+  const int32_t* rowptr;
+  const int32_t* col;
+  int32_t* hist;   // workspace [H][nb][C]
+  int32_t* off;    // workspace [H][nb][C]
+  int32_t* start;  // workspace [H][C]
+  int32_t* perm;   // workspace [H][N]
+  int H, N, C, nb, block, mask_heads;
+};
+
+// Return hipSuccess or the first launch error.
+hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, bool bf16,
+                          hipStream_t stream);
+hipError_t launch_reassign(const ReassignArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// One-time per-process kernel attribute setup (dynamic LDS limits).
+hipError_t prepare_kernels();
+
+}  // namespace da

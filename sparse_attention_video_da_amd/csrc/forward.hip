@@ -1,0 +1,457 @@
+// Fused decoupled sparse attention forward for gfx950.
+//
+// One workgroup owns one (head, query block). It walks the query block's exact key blocks
+// (the plan's sorted list) and then the cluster-cache tiles (C centroid keys / mean values
+// taken BLK at a time), treating both the same way: the tile's keys and values are staged
+// in LDS, scores come from MFMA, and a single online softmax (exp2 domain) absorbs every
+// tile. Cluster tiles add a per-key logit bias log2(n[b][c]) (-inf where n = 0), which in
+// the natural-log domain is the ln-count weight of the DecoupAttn abstract: each cluster
+// stands in for the n of its keys left outside the exact blocks.
+//
+// Work split (bf16): wave w handles 32 query rows. Scores are formed transposed,
+// S^T = K * Q^T, so every lane owns one query column and the row max / row sum need only
+// one cross-half exchange. O^T = V^T * P^T then leaves each lane with the output of the
+// same query, so the online-softmax rescale is a per-lane scalar. V^T operands come
+// straight from the row-major V tile through the gfx950 transposed LDS read.
+#include "da_device.h"
+#include "da_internal.h"
+
+namespace da {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+
+// XCD-aware order: hardware deals workgroup ids round-robin to the 8 XCDs; give each XCD a
+// contiguous range of (head, query block) so neighbouring query blocks, which share many
+// 3D-local key blocks, hit the same L2.
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+  int per = (total + 7) >> 3;
+  return (L & 7) * per + (L >> 3);
+}
+
+// ----------------------------------------------------------------------------- bf16
+template <int D, int BLK>
+__global__ void __launch_bounds__(BLK * 2)
+fwd_bf16_kernel(FwdArgs p) {
+  constexpr int THREADS = BLK * 2;
+  constexpr int KT = BLK / 32;     // 32-key tiles per key block
+  constexpr int DT = D / 32;       // 32-dim tiles of the output
+  constexpr int DS = D / 16;       // k-steps of the score product
+  constexpr int NCH = D / 8;       // 16-byte chunks per row
+  constexpr int TILE = BLK * D * 2;
+  constexpr int PER_T = (BLK * NCH) / THREADS;
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* k_lds = smem;
+  char* v_lds = smem + TILE;
+  float* bias_lds = reinterpret_cast<float*>(smem + 2 * TILE);
+
+  const int total = p.H * p.nb;
+  const int logical = xcd_remap(blockIdx.x, total);
+  if (logical >= total) return;
+  const int h = logical / p.nb;
+  const int b = logical - h * p.nb;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+  const int g = lane >> 4;     // 16-lane group
+  const int gp = lane & 15;
+
+  const uint16_t* Qh = static_cast<const uint16_t*>(p.Q) + (size_t)h * p.N * D;
+  const uint16_t* Kh = static_cast<const uint16_t*>(p.K) + (size_t)h * p.N * D;
+  const uint16_t* Vh = static_cast<const uint16_t*>(p.V) + (size_t)h * p.N * D;
+  const uint16_t* Mh = static_cast<const uint16_t*>(p.mu) + (size_t)h * p.C * D;
+  const uint16_t* Bh = static_cast<const uint16_t*>(p.vbar) + (size_t)h * p.C * D;
+  const int32_t* cnt_row = p.counts + ((size_t)h * p.nb + b) * p.C;
+
+  const int mh = p.mask_heads == 1 ? 0 : h;
+  const int e0 = p.rowptr[mh * (p.nb + 1) + b];
+  const int n_exact = p.rowptr[mh * (p.nb + 1) + b + 1] - e0;
+  const int n_ctile = (p.C + BLK - 1) / BLK;
+  const int ntiles = n_exact + n_ctile;
+
+  // Q^T operand for this lane's query, all d k-steps.
+  const int q = b * BLK + w * 32 + l32;
+  bf16x8 qreg[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    if (q < p.N)
+      qreg[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + 16 * s + 8 * hl);
+    else
+      qreg[s] = bf16x8{};
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -1e30f;   // finite start: exp2(m_run - finite) underflows to 0
+  float l_run = 0.f;      // this half's share of the row sum
+
+  for (int t = 0; t < ntiles; ++t) {
+    const uint16_t* ksrc;
+    const uint16_t* vsrc;
+    int valid, kind;  // kind 0: full exact block, 1: ragged exact block, 2: cluster tile
+    if (t < n_exact) {
+      const int kb = p.col[e0 + t];
+      ksrc = Kh + (size_t)kb * BLK * D;
+      vsrc = Vh + (size_t)kb * BLK * D;
+      valid = min(BLK, p.N - kb * BLK);
+      kind = valid < BLK ? 1 : 0;
+    } else {
+      const int c0 = (t - n_exact) * BLK;
+      ksrc = Mh + (size_t)c0 * D;
+      vsrc = Bh + (size_t)c0 * D;
+      valid = min(BLK, p.C - c0);
+      kind = 2;
+    }
+    // Load the tile to registers before the barrier so the fetch overlaps other waves'
+    // work on the previous tile.
+    bf16x8 kst[PER_T], vst[PER_T];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int idx = i * THREADS + tid;
+      const int row = idx / NCH;
+      const int ch = idx - row * NCH;
+      if (row < valid) {
+        kst[i] = *reinterpret_cast<const bf16x8*>(ksrc + (size_t)row * D + ch * 8);
+        vst[i] = *reinterpret_cast<const bf16x8*>(vsrc + (size_t)row * D + ch * 8);
+      } else {
+        kst[i] = bf16x8{};
+        vst[i] = bf16x8{};
+      }
+    }
+    float bias_v = 0.f;
+    if (kind != 0 && tid < BLK) {
+      if (kind == 1) {
+        bias_v = tid < valid ? 0.f : kNegInf;
+      } else {
+        const int c = (t - n_exact) * BLK + tid;
+        const int n = c < p.C ? cnt_row[c] : 0;
+        bias_v = n > 0 ? fast_log2((float)n) : kNegInf;
+      }
+    }
+    __syncthreads();  // everyone is done reading the previous tile
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int idx = i * THREADS + tid;
+      const int row = idx / NCH;
+      const int ch = idx - row * NCH;
+      *reinterpret_cast<bf16x8*>(k_lds + swz_byte<D>(row, ch)) = kst[i];
+      *reinterpret_cast<bf16x8*>(v_lds + swz_byte<D>(row, ch)) = vst[i];
+    }
+    if (kind != 0 && tid < BLK) bias_lds[tid] = bias_v;
+    __syncthreads();
+
+    // S^T tile: rows = keys, columns = this wave's 32 queries.
+    f32x16 sacc[KT];
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 a = lds_read_b128(k_lds, swz_byte<D>(32 * mk + l32, 2 * s + hl));
+        acc = mfma32x32x16(a, qreg[s], acc);
+      }
+      sacc[mk] = acc;
+    }
+
+    // Online softmax in the exp2 domain.
+    float mloc = kNegInf;
+    if (kind == 0) {
+#pragma unroll
+      for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[mk][r] * p.scale_log2e;
+          sacc[mk][r] = x;
+          mloc = fmaxf(mloc, x);
+        }
+    } else {
+#pragma unroll
+      for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_lds + 32 * mk + 8 * i + 4 * hl);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = sacc[mk][4 * i + j] * p.scale_log2e + bv[j];
+            sacc[mk][4 * i + j] = x;
+            mloc = fmaxf(mloc, x);
+          }
+        }
+    }
+    const float m_new = fmaxf(m_run, fmaxf(mloc, xor32(mloc)));
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(sacc[mk][r] - m_new);
+        sacc[mk][r] = e;
+        lsum += e;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+    // O^T += V^T P^T. k-step (mk, t2) covers keys 32mk + 16t2 + {0..15}; this lane's
+    // eight k-values are keys 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3), which are
+    // exactly its score accumulators 8t2 .. 8t2+7.
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[mk][8 * t2 + e];
+        const int vrow = 32 * mk + 16 * t2 + 4 * (g >> 1) + (gp >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int col = 32 * dt + 16 * (g & 1) + 4 * (gp & 3);
+          const int cb = ((col & 7) << 1);
+          const bf16x4 lo = lds_read_tr16(v_lds, swz_byte<D>(vrow, col >> 3) + cb);
+          const bf16x4 hi = lds_read_tr16(v_lds, swz_byte<D>(vrow + 8, col >> 3) + cb);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
+        }
+      }
+  }
+
+  // Epilogue: normalise and store. Lane holds O[q][32dt + 8i + 4hl + j].
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = 1.f / l_tot;
+  if (q < p.N) {
+    uint16_t* orow = static_cast<uint16_t*>(p.O) + ((size_t)h * p.N + q) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * i + 0] * inv) |
+                      ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * i + 1] * inv) << 16);
+        uint32_t hi = (uint32_t)f32_to_bf16_rne(oacc[dt][4 * i + 2] * inv) |
+                      ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * i + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i + 4 * hl) = make_uint2(lo, hi);
+      }
+    if (p.lse != nullptr && hl == 0)
+      p.lse[(size_t)h * p.N + q] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------------------- fp32
+// Same structure with the fp32 32x32x2 MFMA (full fp32 products). K rows are padded by one
+// float and V rows by four so the column-wise operand reads do not pile onto one bank.
+template <int D, int BLK>
+__global__ void __launch_bounds__(BLK * 2)
+fwd_f32_kernel(FwdArgs p) {
+  constexpr int THREADS = BLK * 2;
+  constexpr int KT = BLK / 32;
+  constexpr int DT = D / 32;
+  constexpr int KS = D / 2;
+  constexpr int KST = D + 1;
+  constexpr int VST = D + 4;
+  constexpr int NC4 = D / 4;
+  constexpr int PER_T = (BLK * NC4) / THREADS;
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* k_lds = reinterpret_cast<float*>(smem);
+  float* v_lds = k_lds + BLK * KST;
+  float* bias_lds = v_lds + BLK * VST;
+
+  const int total = p.H * p.nb;
+  const int logical = xcd_remap(blockIdx.x, total);
+  if (logical >= total) return;
+  const int h = logical / p.nb;
+  const int b = logical - h * p.nb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  const float* Qh = static_cast<const float*>(p.Q) + (size_t)h * p.N * D;
+  const float* Kh = static_cast<const float*>(p.K) + (size_t)h * p.N * D;
+  const float* Vh = static_cast<const float*>(p.V) + (size_t)h * p.N * D;
+  const float* Mh = static_cast<const float*>(p.mu) + (size_t)h * p.C * D;
+  const float* Bh = static_cast<const float*>(p.vbar) + (size_t)h * p.C * D;
+  const int32_t* cnt_row = p.counts + ((size_t)h * p.nb + b) * p.C;
+  const int mh = p.mask_heads == 1 ? 0 : h;
+  const int e0 = p.rowptr[mh * (p.nb + 1) + b];
+  const int n_exact = p.rowptr[mh * (p.nb + 1) + b + 1] - e0;
+  const int ntiles = n_exact + (p.C + BLK - 1) / BLK;
+
+  const int q = b * BLK + w * 32 + l32;
+  float qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qreg[s] = q < p.N ? Qh[(size_t)q * D + 2 * s + hl] : 0.f;
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const float *ksrc, *vsrc;
+    int valid, kind;
+    if (t < n_exact) {
+      const int kb = p.col[e0 + t];
+      ksrc = Kh + (size_t)kb * BLK * D;
+      vsrc = Vh + (size_t)kb * BLK * D;
+      valid = min(BLK, p.N - kb * BLK);
+      kind = valid < BLK ? 1 : 0;
+    } else {
+      const int c0 = (t - n_exact) * BLK;
+      ksrc = Mh + (size_t)c0 * D;
+      vsrc = Bh + (size_t)c0 * D;
+      valid = min(BLK, p.C - c0);
+      kind = 2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int idx = i * THREADS + tid;
+      const int row = idx / NC4;
+      const int c4 = idx - row * NC4;
+      f32x4 kv = f32x4{}, vv = f32x4{};
+      if (row < valid) {
+        kv = *reinterpret_cast<const f32x4*>(ksrc + (size_t)row * D + 4 * c4);
+        vv = *reinterpret_cast<const f32x4*>(vsrc + (size_t)row * D + 4 * c4);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k_lds[row * KST + 4 * c4 + e] = kv[e];
+        v_lds[row * VST + 4 * c4 + e] = vv[e];
+      }
+    }
+    if (tid < BLK) {
+      float bv = 0.f;
+      if (kind == 1) bv = tid < valid ? 0.f : kNegInf;
+      if (kind == 2) {
+        const int c = (t - n_exact) * BLK + tid;
+        const int n = c < p.C ? cnt_row[c] : 0;
+        bv = n > 0 ? fast_log2((float)n) : kNegInf;
+      }
+      bias_lds[tid] = bv;
+    }
+    __syncthreads();
+
+    f32x16 sacc[KT];
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = mfma32x32x2(k_lds[(32 * mk + l32) * KST + 2 * s + hl], qreg[s], acc);
+      sacc[mk] = acc;
+    }
+    float mloc = kNegInf;
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * mk + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float x = sacc[mk][r] * p.scale_log2e + bias_lds[key];
+        sacc[mk][r] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    const float m_new = fmaxf(m_run, fmaxf(mloc, xor32(mloc)));
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(sacc[mk][r] - m_new);
+        sacc[mk][r] = e;
+        lsum += e;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    // O^T += V^T P^T: the k-pair (mk, r) is keys 32mk + 8(r/4) + (r%4) (lower half) and
+    // +4 (upper half), which are exactly the lane's score accumulator r.
+#pragma unroll
+    for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * mk + 8 * (r >> 2) + 4 * hl + (r & 3);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          oacc[dt] = mfma32x32x2(v_lds[key * VST + 32 * dt + l32], sacc[mk][r], oacc[dt]);
+      }
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  if (q < p.N) {
+    float* orow = static_cast<float*>(p.O) + ((size_t)h * p.N + q) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = oacc[dt][4 * i + j] / l_tot;
+        *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * i + 4 * hl) = o;
+      }
+    if (p.lse != nullptr && hl == 0)
+      p.lse[(size_t)h * p.N + q] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------------------- launch
+template <int D, int BLK>
+static size_t fwd_lds_bytes(bool bf16) {
+  return bf16 ? (size_t)2 * BLK * D * 2 + BLK * 4
+              : (size_t)BLK * (D + 1) * 4 + (size_t)BLK * (D + 4) * 4 + BLK * 4;
+}
+
+template <int D, int BLK>
+static hipError_t launch_fwd_t(const FwdArgs& a, bool bf16, hipStream_t stream) {
+  const int total = a.H * a.nb;
+  const int grid = ((total + 7) / 8) * 8;
+  const size_t lds = fwd_lds_bytes<D, BLK>(bf16);
+  if (bf16)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 2), lds, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<D, BLK>), dim3(grid), dim3(BLK * 2), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, bool bf16,
+                          hipStream_t stream) {
+  if (head_dim == 64 && block == 64) return launch_fwd_t<64, 64>(a, bf16, stream);
+  if (head_dim == 64 && block == 128) return launch_fwd_t<64, 128>(a, bf16, stream);
+  if (head_dim == 128 && block == 64) return launch_fwd_t<128, 64>(a, bf16, stream);
+  if (head_dim == 128 && block == 128) return launch_fwd_t<128, 128>(a, bf16, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D, int BLK>
+static hipError_t prep_fwd() {
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fwd_bf16_kernel<D, BLK>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)fwd_lds_bytes<D, BLK>(true));
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32_kernel<D, BLK>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)fwd_lds_bytes<D, BLK>(false));
+}
+
+hipError_t prepare_forward_kernels() {
+  hipError_t e;
+  if ((e = prep_fwd<64, 64>()) != hipSuccess) return e;
+  if ((e = prep_fwd<64, 128>()) != hipSuccess) return e;
+  if ((e = prep_fwd<128, 64>()) != hipSuccess) return e;
+  return prep_fwd<128, 128>();
+}
+
+}  // namespace da

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Stage-wise and teacher-forced in the oracle -> GPU direction only: the forward is fed the
+oracle's refreshed cache, the reassign the seeded (or oracle-warmed) cache; nothing the
+GPU produced is ever an oracle input. Sizes span several tiles with ragged tails.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from datagen import block_mask, get_config, make_layer, drift_layer
+from parity_util import (check_forward, check_reassign_head, from_dev, say, store64,
+                         to_dev, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_video_da_amd as S
+    return S
+
+
+def _layer64(L, dtype):
+    return {x: np.stack([O.to_f64(L[x][i], dtype) for i in range(L[x].shape[0])])
+            for x in ("Q", "K", "V")}
+
+
+def _random_layer(seed, H, N, d, dtype, C, G=None, sigma=0.3):
+    """Mixture-shaped Q/K, N(0,1) V, stored in dtype (for shapes the named configs lack)."""
+    rng = np.random.default_rng(seed)
+    G = G or max(2, C // 2)
+    out = {}
+    for x in ("Q", "K"):
+        arr = []
+        for h in range(H):
+            cen = rng.standard_normal((G, d)).astype(np.float32)
+            arr.append(cen[rng.integers(0, G, N)] + np.float32(sigma) *
+                       rng.standard_normal((N, d)).astype(np.float32))
+        out[x] = np.stack(arr)
+    out["V"] = rng.standard_normal((H, N, d)).astype(np.float32)
+    if dtype == "bf16":
+        from datagen import f32_to_bf16_bits
+        out = {k: f32_to_bf16_bits(v) for k, v in out.items()}
+    cache = np.stack([out["K"][h][np.sort(rng.choice(N, C, replace=False))] for h in range(H)])
+    return out, cache
+
+
+def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=None):
+    """GPU reassign + forward vs the oracle on the given heads (default: all)."""
+    torch = torch_mod()
+    H, N, d, B, C, dtype = (cfgd[k] for k in ("H", "N", "d", "B", "C", "dtype"))
+    heads = list(range(H)) if heads is None else heads
+    say(f"[case] {what}: H={H} N={N} d={d} B={B} C={C} {dtype} exact={int(mask.sum())}")
+    plan = lib.Plan(H, N, d, B, C, mask, dtype=dtype)
+    dev = {x: to_dev(L[x], dtype) for x in ("Q", "K", "V")}
+    mu0 = to_dev(mu0_stored, dtype)
+    L64 = _layer64(L, dtype)
+    mu0_64 = np.stack([O.to_f64(mu0_stored[h], dtype) for h in range(H)])
+    mask_h = (lambda h: mask[0] if mask.shape[0] == 1 else mask[h])
+    if check_reassign:
+        out = plan.reassign(dev["K"], dev["V"], mu0)
+        torch.cuda.synchronize()
+        got = {"assign": out["assign"].cpu().numpy(), "sizes": out["sizes"].cpu().numpy(),
+               "counts": out["counts"].cpu().numpy(),
+               "centroids": from_dev(out["centroids"], dtype),
+               "mean_values": from_dev(out["mean_values"], dtype)}
+        moves = 0
+        for h in heads:
+            r = check_reassign_head(L64["K"][h], L64["V"][h], mu0_64[h], mask_h(h), B, dtype,
+                                    {k: v[h] for k, v in got.items()}, f"{what} head {h}")
+            moves += r["band_moves"]
+        say(f"  reassign ok ({len(heads)} heads, {moves} in-band moves)")
+    # forward, teacher-forced with the oracle's refreshed cache
+    caches = {h: O.reassign_step(L64["K"][h], L64["V"][h], mu0_64[h], mask_h(h), B, dtype)
+              for h in heads}
+    mu1 = np.zeros((H, C, d), np.float32 if dtype == "f32" else np.uint16)
+    vb = np.zeros_like(mu1)
+    cnt = np.zeros((H, plan.num_blocks, C), np.int32)
+    for h in heads:
+        mu1[h] = store64(caches[h]["mu1"], dtype)
+        vb[h] = store64(caches[h]["vbar"], dtype)
+        cnt[h] = caches[h]["counts"]
+    o_dev, lse_dev = plan.forward(dev["Q"], dev["K"], dev["V"], to_dev(mu1, dtype),
+                                  to_dev(vb, dtype), torch.from_numpy(cnt).cuda(), lse=True)
+    torch.cuda.synchronize()
+    o = from_dev(o_dev, dtype)
+    lse = lse_dev.cpu().numpy().astype(np.float64)
+    got_all, want_all, lg, lw = [], [], [], []
+    for h in heads:
+        ref_o, ref_lse = O.forward(L64["Q"][h], L64["K"][h], L64["V"][h], caches[h]["mu1"],
+                                   caches[h]["vbar"], caches[h]["counts"], mask_h(h), B)
+        got_all.append(o[h])
+        want_all.append(ref_o)
+        lg.append(lse[h])
+        lw.append(ref_lse)
+    check_forward(np.concatenate(got_all), np.concatenate(want_all), dtype, f"{what} forward")
+    np.testing.assert_allclose(np.concatenate(lg), np.concatenate(lw), rtol=0,
+                               atol=1e-3 if dtype == "bf16" else 1e-5)
+    plan.close()
+    return o, caches
+
+
+def _cfgd(cfg, H=None):
+    return dict(H=H or cfg.heads, N=cfg.seq_len, d=cfg.head_dim, B=cfg.block, C=cfg.clusters,
+                dtype=cfg.dtype)
+
+
+# ----------------------------------------------------------------- named small configs
+def test_tiny_f32_config(lib):
+    """1 head, N=1024, d=64, fp32, 16 clusters, diagonal + 3 random blocks; the cache is
+    warmed by 10 oracle Lloyd iterations on the pre-drift keys, then K drifts."""
+    cfg = get_config("tiny_f32")
+    L = make_layer(cfg)
+    mu0 = np.stack([O.lloyd_warmup(O.to_f64(L["K"][h], "f32"), O.to_f64(L["cache_init"][h], "f32"),
+                                   10, "f32") for h in range(cfg.heads)]).astype(np.float32)
+    L1 = drift_layer(cfg, L, 0)
+    _run_case(lib, L1, mu0, L["mask"], _cfgd(cfg), "tiny_f32")
+
+
+def test_small_bf16_config(lib):
+    """12 heads, N=4096, d=64, bf16, C=64, 25% 3D-local mask, oracle-warmed cache."""
+    cfg = get_config("small_bf16")
+    L = make_layer(cfg)
+    mu0 = np.stack([store64(O.lloyd_warmup(O.to_f64(L["K"][h], "bf16"),
+                                           O.to_f64(L["cache_init"][h], "bf16"), 10, "bf16"),
+                            "bf16") for h in range(cfg.heads)])
+    _run_case(lib, L, mu0, L["mask"], _cfgd(cfg), "small_bf16")
+
+
+# ----------------------------------------------------------------- ragged / edge shapes
+@pytest.mark.parametrize("d,B,dtype", [(128, 128, "bf16"), (64, 128, "bf16"), (128, 64, "bf16"),
+                                       (64, 64, "bf16"), (128, 128, "f32"), (64, 64, "f32")])
+def test_ragged_shapes(lib, d, B, dtype):
+    """N = 1000 (ragged last block), C = 200 (ragged cluster tile), random 30% mask with one
+    empty row and one full row, 2 heads with per-head masks."""
+    H, N, C = 2, 1000, 200
+    L, cache = _random_layer(100 + d + B, H, N, d, dtype, C)
+    nb = -(-N // B)
+    rng = np.random.default_rng(7)
+    mask = (rng.random((H, nb, nb)) < 0.3).astype(np.uint8)
+    mask[0, 1, :] = 0
+    mask[1, 2, :] = 1
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype=dtype),
+              f"ragged d{d} B{B} {dtype}")
+
+
+def test_all_blocks_exact_is_dense(lib):
+    """Every block exact: the GPU output is dense attention (oracle's dense routine)."""
+    torch = torch_mod()
+    H, N, d, B, C = 1, 700, 128, 128, 8
+    L, cache = _random_layer(5, H, N, d, "bf16", C)
+    nb = -(-N // B)
+    mask = np.ones((1, nb, nb), np.uint8)
+    plan = lib.Plan(H, N, d, B, C, mask)
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], to_dev(cache, "bf16"))
+    assert int(out["counts"].abs().sum().item()) == 0
+    o = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"],
+                     out["counts"])
+    torch.cuda.synchronize()
+    L64 = _layer64(L, "bf16")
+    want = O.dense_attention(L64["Q"][0], L64["K"][0], L64["V"][0])
+    check_forward(from_dev(o, "bf16")[0], want, "bf16", "all-exact vs dense")
+
+
+def test_one_cluster_per_key_is_dense(lib):
+    """C = N with the cache at the keys: any mask gives dense attention."""
+    torch = torch_mod()
+    H, N, d, B = 1, 300, 64, 64
+    L, _ = _random_layer(6, H, N, d, "bf16", 4)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(3).random((1, nb, nb)) < 0.4).astype(np.uint8)
+    plan = lib.Plan(H, N, d, B, N, mask)
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], dev["K"].clone())
+    o = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"],
+                     out["counts"])
+    torch.cuda.synchronize()
+    assert out["assign"].cpu().numpy().tolist() == [list(range(N))]
+    L64 = _layer64(L, "bf16")
+    want = O.dense_attention(L64["Q"][0], L64["K"][0], L64["V"][0])
+    check_forward(from_dev(o, "bf16")[0], want, "bf16", "C=N vs dense")
+
+
+def test_empty_mask_one_cluster_is_mean(lib):
+    """No exact block, one cluster: every row is the mean of V (closed form)."""
+    torch = torch_mod()
+    H, N, d, B = 2, 520, 128, 128
+    L, cache = _random_layer(8, H, N, d, "bf16", 1)
+    nb = -(-N // B)
+    plan = lib.Plan(H, N, d, B, 1, np.zeros((1, nb, nb), np.uint8))
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], to_dev(cache, "bf16"))
+    o = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"],
+                     out["counts"])
+    torch.cuda.synchronize()
+    V64 = _layer64(L, "bf16")["V"]
+    for h in range(H):
+        want = np.broadcast_to(V64[h].mean(axis=0), (N, d))
+        check_forward(from_dev(o, "bf16")[h], want, "bf16", f"empty mask C=1 head {h}")
+
+
+def test_plan_exact_lists_match_mask(lib):
+    cfg = get_config("wan14b_bf16")
+    mask = block_mask(cfg)
+    plan = lib.Plan(2, cfg.seq_len, 128, 128, 256, mask)
+    rowptr, col = plan.exact_lists(0)
+    nb = cfg.num_blocks
+    assert rowptr[-1] == int(mask.sum())
+    for b in range(nb):
+        assert col[rowptr[b]:rowptr[b + 1]].tolist() == np.nonzero(mask[0, b])[0].tolist()
+    info = plan.info()
+    assert info["num_blocks"] == nb and info["exact_pairs"] == int(mask.sum())
+    plan.close()
+
+
+def test_entry_point_validation_on_device(lib):
+    """Aliased cache buffers and misaligned pointers are rejected before any launch."""
+    torch = torch_mod()
+    H, N, d, B, C = 1, 256, 64, 64, 8
+    plan = lib.Plan(H, N, d, B, C, np.ones((1, 4, 4), np.uint8))
+    K = torch.zeros((H, N, d), dtype=torch.bfloat16, device="cuda")
+    mu = torch.zeros((H, C, d), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.zeros((H, C, d), dtype=torch.bfloat16, device="cuda"),
+            torch.zeros((H, N), dtype=torch.int32, device="cuda"),
+            torch.zeros((H, C), dtype=torch.int32, device="cuda"),
+            torch.zeros((H, 4, C), dtype=torch.int32, device="cuda")]
+    st = lib.da_reassign(plan._h, K.data_ptr(), K.data_ptr(), mu.data_ptr(), mu.data_ptr(),
+                         outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                         outs[3].data_ptr(), None)
+    assert st == lib.DA_ERR_INVALID_ARGUMENT
+    st = lib.da_forward(plan._h, K.data_ptr() + 2, K.data_ptr(), K.data_ptr(), mu.data_ptr(),
+                        mu.data_ptr(), outs[3].data_ptr(), K.data_ptr(), None, None)
+    assert st == lib.DA_ERR_INVALID_ARGUMENT
+    st = lib.da_forward(plan._h, None, K.data_ptr(), K.data_ptr(), mu.data_ptr(),
+                        mu.data_ptr(), outs[3].data_ptr(), K.data_ptr(), None, None)
+    assert st == lib.DA_ERR_INVALID_ARGUMENT
+    plan.close()
