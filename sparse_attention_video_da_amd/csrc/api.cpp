@@ -23,8 +23,15 @@ struct da_plan_s {
   float scale;
   std::vector<int32_t> rowptr;  // [mask_heads][nb + 1], absolute offsets into col
   std::vector<int32_t> col;
+  // query-block pairs (2p, 2p+1): ascending union of both exact lists, each entry
+  // kb | (kb exact for 2p) << 28 | (kb exact for 2p+1) << 29
+  std::vector<int32_t> prowptr;  // [mask_heads][npairs + 1]
+  std::vector<int32_t> pcol;
+  int32_t npairs = 0;
   int32_t* d_rowptr = nullptr;
   int32_t* d_col = nullptr;
+  int32_t* d_prowptr = nullptr;
+  int32_t* d_pcol = nullptr;
   int32_t* d_hist = nullptr;
   int32_t* d_off = nullptr;
   int32_t* d_start = nullptr;
@@ -66,10 +73,12 @@ da_status check_desc(const da_desc* d) {
 }
 
 void destroy_device(da_plan_s* p) {
-  int32_t* bufs[] = {p->d_rowptr, p->d_col, p->d_hist, p->d_off, p->d_start, p->d_perm};
+  int32_t* bufs[] = {p->d_rowptr, p->d_col,   p->d_prowptr, p->d_pcol,
+                     p->d_hist,   p->d_off,   p->d_start,   p->d_perm};
   for (int32_t* b : bufs)
     if (b) (void)hipFree(b);
-  p->d_rowptr = p->d_col = p->d_hist = p->d_off = p->d_start = p->d_perm = nullptr;
+  p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
+  p->d_hist = p->d_off = p->d_start = p->d_perm = nullptr;
 }
 
 std::once_flag g_prep_once;
@@ -122,6 +131,22 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
     }
     p->rowptr[(size_t)mh * (nb + 1) + nb] = (int32_t)p->col.size();
   }
+  const int32_t npairs = (nb + 1) / 2;
+  p->npairs = npairs;
+  p->prowptr.resize((size_t)desc->mask_heads * (npairs + 1));
+  for (int32_t mh = 0; mh < desc->mask_heads; ++mh) {
+    const uint8_t* m = mask + (size_t)mh * nb * nb;
+    for (int32_t pr = 0; pr < npairs; ++pr) {
+      p->prowptr[(size_t)mh * (npairs + 1) + pr] = (int32_t)p->pcol.size();
+      const int32_t b0 = 2 * pr, b1 = 2 * pr + 1;
+      for (int32_t kb = 0; kb < nb; ++kb) {
+        const int32_t f0 = m[(size_t)b0 * nb + kb] ? 1 : 0;
+        const int32_t f1 = (b1 < nb && m[(size_t)b1 * nb + kb]) ? 1 : 0;
+        if (f0 | f1) p->pcol.push_back(kb | (f0 << 28) | (f1 << 29));
+      }
+    }
+    p->prowptr[(size_t)mh * (npairs + 1) + npairs] = (int32_t)p->pcol.size();
+  }
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1 || hipGetDevice(&p->device) != hipSuccess) {
@@ -139,9 +164,11 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
 
   const size_t H = desc->heads, N = desc->seq_len, C = desc->clusters;
   const size_t n_rowptr = p->rowptr.size(), n_col = std::max<size_t>(1, p->col.size());
+  const size_t n_prowptr = p->prowptr.size(), n_pcol = std::max<size_t>(1, p->pcol.size());
   struct Alloc { int32_t** ptr; size_t n; } allocs[] = {
-      {&p->d_rowptr, n_rowptr}, {&p->d_col, n_col},        {&p->d_hist, H * nb * C},
-      {&p->d_off, H * nb * C},  {&p->d_start, H * C},      {&p->d_perm, H * N}};
+      {&p->d_rowptr, n_rowptr},   {&p->d_col, n_col},   {&p->d_prowptr, n_prowptr},
+      {&p->d_pcol, n_pcol},       {&p->d_hist, H * nb * C}, {&p->d_off, H * nb * C},
+      {&p->d_start, H * C},       {&p->d_perm, H * N}};
   for (const Alloc& a : allocs) {
     if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -154,7 +181,11 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
   if (hipMemcpy(p->d_rowptr, p->rowptr.data(), n_rowptr * sizeof(int32_t),
                 hipMemcpyHostToDevice) != hipSuccess ||
       (!p->col.empty() && hipMemcpy(p->d_col, p->col.data(), p->col.size() * sizeof(int32_t),
-                                    hipMemcpyHostToDevice) != hipSuccess)) {
+                                    hipMemcpyHostToDevice) != hipSuccess) ||
+      hipMemcpy(p->d_prowptr, p->prowptr.data(), n_prowptr * sizeof(int32_t),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      (!p->pcol.empty() && hipMemcpy(p->d_pcol, p->pcol.data(), p->pcol.size() * sizeof(int32_t),
+                                     hipMemcpyHostToDevice) != hipSuccess)) {
     destroy_device(p);
     delete p;
     return DA_ERR_DEVICE;
@@ -260,6 +291,9 @@ DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void*
   a.counts = qblock_counts;
   a.rowptr = p->d_rowptr;
   a.col = p->d_col;
+  a.prowptr = p->d_prowptr;
+  a.pcol = p->d_pcol;
+  a.npairs = p->npairs;
   a.O = O;
   a.lse = lse_out;
   a.H = d.heads;

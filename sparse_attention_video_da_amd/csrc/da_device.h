@@ -31,14 +31,19 @@ __device__ __forceinline__ f32x16 mfma32x32x2(float a, float b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------------------- LDS tiles
-// A bf16 tile of R rows x D columns is stored row-major with its 16-byte chunks XOR-
-// swizzled by the row index (chunk' = chunk ^ (row % (D/8))), so that 32 lanes reading the
-// same logical chunk of 32 consecutive rows, or the transposed 8-byte reads of a few
-// rows, spread over the LDS banks.
+// A bf16 tile of R rows x D columns is stored row-major in 16-byte chunks, chunk c of row r
+// at physical chunk c ^ swz_key<D>(r). For D = 128 (16 chunks, rows 256 B apart) the key is
+// a bijection on 0..15 over any 16 consecutive rows (32 lanes reading one logical chunk of
+// consecutive rows spread over all banks) and gives 4 consecutive rows disjoint 4-chunk
+// groups (the transposed 8-byte reads of 4 rows x 4 chunks hit 16 distinct bank groups).
+template <int D>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (row >> 1) & 7;
+}
 template <int D>
 __device__ __forceinline__ int swz_byte(int row, int chunk) {
-  constexpr int NCH = D / 8;
-  return row * (D * 2) + ((chunk ^ (row % NCH)) << 4);
+  return row * (D * 2) + ((chunk ^ swz_key<D>(row)) << 4);
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int byte_off) {

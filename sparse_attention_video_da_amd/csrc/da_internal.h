@@ -16,6 +16,9 @@ struct FwdArgs {
   const int32_t* counts; // [H][nb][C]
   const int32_t* rowptr; // [mask_heads][nb + 1], absolute offsets into col
   const int32_t* col;    // sorted exact key blocks
+  const int32_t* prowptr; // [mask_heads][npairs + 1] lists of query-block pairs (2p, 2p+1)
+  const int32_t* pcol;    // union of the pair's exact blocks: kb | (in 2p) << 28 | (in 2p+1) << 29
+  int npairs;
   void* O;
   float* lse;            // may be null
   int H, N, C, nb, mask_heads;

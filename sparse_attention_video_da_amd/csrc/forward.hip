@@ -30,51 +30,133 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
 }
 
 // ----------------------------------------------------------------------------- bf16
+// A workgroup owns two adjacent query blocks (2p, 2p+1) of one head: BLK/32 waves per
+// block. It walks the ascending union of the two exact lists, so a key block both blocks
+// keep exact is fetched once (neighbouring query blocks of a 3D-local mask share most of
+// their key blocks), then the cluster tiles, which both blocks use with their own bias
+// rows. A wave skips the tiles its block does not keep.
+struct TileDesc {
+  const uint16_t* k;
+  const uint16_t* v;
+  int valid;  // rows that exist (keys < N, or clusters < C)
+  int kind;   // 0 full exact block, 1 ragged exact block, 2 cluster tile
+  int c0;     // first cluster of a cluster tile
+  int use;    // bit h: query block 2p+h uses this tile
+};
+
 template <int D, int BLK>
-__global__ void __launch_bounds__(BLK * 2)
+__device__ __forceinline__ TileDesc tile_desc(const FwdArgs& p, int t, int n_list, int e0,
+                                              const uint16_t* Kh, const uint16_t* Vh,
+                                              const uint16_t* Mh, const uint16_t* Bh) {
+  TileDesc d;
+  if (t < n_list) {
+    const int entry = p.pcol[e0 + t];
+    const int kb = entry & 0x0fffffff;
+    d.k = Kh + (size_t)kb * BLK * D;
+    d.v = Vh + (size_t)kb * BLK * D;
+    d.valid = min(BLK, p.N - kb * BLK);
+    d.kind = d.valid < BLK ? 1 : 0;
+    d.c0 = 0;
+    d.use = (entry >> 28) & 3;
+  } else {
+    d.c0 = (t - n_list) * BLK;
+    d.k = Mh + (size_t)d.c0 * D;
+    d.v = Bh + (size_t)d.c0 * D;
+    d.valid = min(BLK, p.C - d.c0);
+    d.kind = 2;
+    d.use = 3;
+  }
+  return d;
+}
+
+// Direct-to-LDS fetch of one K or V tile by THREADS threads: each wave instruction fills
+// 1 KB of consecutive 16-byte LDS slots; the lane filling physical slot (row, pc) reads
+// logical chunk pc ^ swz_key(row) of that row. Rows past `valid` re-read the last valid
+// row: their logits are masked to -inf, so their contents only need to be finite.
+template <int D, int BLK, int THREADS>
+__device__ __forceinline__ void fetch_tile(const uint16_t* src, int valid, char* lds_tile,
+                                           int tid, int wave) {
+  constexpr int NCH = D / 8;
+  constexpr int PER_T = (BLK * NCH) / THREADS;
+  static_assert(PER_T * THREADS == BLK * NCH, "tile must split evenly");
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int slot = i * THREADS + tid;
+    const int row = slot / NCH;
+    const int pc = slot - row * NCH;
+    const int c = pc ^ swz_key<D>(row);
+    const int srow = min(row, valid - 1);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(src + (size_t)srow * D + c * 8),
+        (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + wave * 64) * 16),
+        16, 0, 0);
+  }
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdArgs p) {
-  constexpr int THREADS = BLK * 2;
+  constexpr int THREADS = BLK * 4;
+  constexpr int WPB = BLK / 32;    // waves per query block
   constexpr int KT = BLK / 32;     // 32-key tiles per key block
   constexpr int DT = D / 32;       // 32-dim tiles of the output
   constexpr int DS = D / 16;       // k-steps of the score product
-  constexpr int NCH = D / 8;       // 16-byte chunks per row
   constexpr int TILE = BLK * D * 2;
-  constexpr int PER_T = (BLK * NCH) / THREADS;
+  constexpr float kRescale = 8.f;  // log2 headroom before the running max is moved
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* k_lds = smem;
-  char* v_lds = smem + TILE;
-  float* bias_lds = reinterpret_cast<float*>(smem + 2 * TILE);
+  // stage s: K at 2*s*TILE, V at (2*s+1)*TILE; then bias rows [stage][half][BLK]
+  float* bias_base = reinterpret_cast<float*>(smem + 4 * TILE);
 
-  const int total = p.H * p.nb;
+  const int total = p.H * p.npairs;
   const int logical = xcd_remap(blockIdx.x, total);
   if (logical >= total) return;
-  const int h = logical / p.nb;
-  const int b = logical - h * p.nb;
+  const int h = logical / p.npairs;
+  const int pr = logical - h * p.npairs;
+  const int b0 = 2 * pr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int half = w / WPB;
+  const int wq = w - half * WPB;
   const int hl = lane >> 5;
   const int l32 = lane & 31;
-  const int g = lane >> 4;     // 16-lane group
+  const int g = lane >> 4;
   const int gp = lane & 15;
+  const int bw = b0 + half;
+  const bool block_ok = bw < p.nb;
 
   const uint16_t* Qh = static_cast<const uint16_t*>(p.Q) + (size_t)h * p.N * D;
   const uint16_t* Kh = static_cast<const uint16_t*>(p.K) + (size_t)h * p.N * D;
   const uint16_t* Vh = static_cast<const uint16_t*>(p.V) + (size_t)h * p.N * D;
   const uint16_t* Mh = static_cast<const uint16_t*>(p.mu) + (size_t)h * p.C * D;
   const uint16_t* Bh = static_cast<const uint16_t*>(p.vbar) + (size_t)h * p.C * D;
-  const int32_t* cnt_row = p.counts + ((size_t)h * p.nb + b) * p.C;
 
   const int mh = p.mask_heads == 1 ? 0 : h;
-  const int e0 = p.rowptr[mh * (p.nb + 1) + b];
-  const int n_exact = p.rowptr[mh * (p.nb + 1) + b + 1] - e0;
-  const int n_ctile = (p.C + BLK - 1) / BLK;
-  const int ntiles = n_exact + n_ctile;
+  const int e0 = p.prowptr[mh * (p.npairs + 1) + pr];
+  const int n_list = p.prowptr[mh * (p.npairs + 1) + pr + 1] - e0;
+  const int ntiles = n_list + (p.C + BLK - 1) / BLK;
+
+  // Bias rows (log2 domain) of a tile, thread tid < 2*BLK fills [tid / BLK][tid % BLK]:
+  // 0 / -inf past N for a ragged exact block, log2 n[b][c] or -inf for a cluster tile.
+  auto tile_bias = [&](const TileDesc& d) -> float {
+    const int hb = tid / BLK, r = tid - hb * BLK;
+    if (d.kind == 1) return r < d.valid ? 0.f : kNegInf;
+    const int bq = b0 + hb;
+    const int c = d.c0 + r;
+    const int n = (c < p.C && bq < p.nb) ? p.counts[((size_t)h * p.nb + bq) * p.C + c] : 0;
+    return n > 0 ? fast_log2((float)n) : kNegInf;
+  };
+
+  // prologue: tile 0 into stage 0
+  TileDesc cur = tile_desc<D, BLK>(p, 0, n_list, e0, Kh, Vh, Mh, Bh);
+  fetch_tile<D, BLK, THREADS>(cur.k, cur.valid, smem, tid, w);
+  fetch_tile<D, BLK, THREADS>(cur.v, cur.valid, smem + TILE, tid, w);
+  if (cur.kind != 0 && tid < 2 * BLK) bias_base[tid] = tile_bias(cur);
 
   // Q^T operand for this lane's query, all d k-steps.
-  const int q = b * BLK + w * 32 + l32;
+  const int q = bw * BLK + wq * 32 + l32;
   bf16x8 qreg[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
@@ -87,141 +169,129 @@ fwd_bf16_kernel(FwdArgs p) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-  float m_run = -1e30f;   // finite start: exp2(m_run - finite) underflows to 0
-  float l_run = 0.f;      // this half's share of the row sum
+  float m_run = -1e30f;   // reference max (log2 domain); finite so exp2(m_run - x) is safe
+  float l_run = 0.f;      // this half-wave's share of the row sum
+  const float c2 = p.scale_log2e;
+  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const uint16_t* ksrc;
-    const uint16_t* vsrc;
-    int valid, kind;  // kind 0: full exact block, 1: ragged exact block, 2: cluster tile
-    if (t < n_exact) {
-      const int kb = p.col[e0 + t];
-      ksrc = Kh + (size_t)kb * BLK * D;
-      vsrc = Vh + (size_t)kb * BLK * D;
-      valid = min(BLK, p.N - kb * BLK);
-      kind = valid < BLK ? 1 : 0;
-    } else {
-      const int c0 = (t - n_exact) * BLK;
-      ksrc = Mh + (size_t)c0 * D;
-      vsrc = Bh + (size_t)c0 * D;
-      valid = min(BLK, p.C - c0);
-      kind = 2;
-    }
-    // Load the tile to registers before the barrier so the fetch overlaps other waves'
-    // work on the previous tile.
-    bf16x8 kst[PER_T], vst[PER_T];
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = i * THREADS + tid;
-      const int row = idx / NCH;
-      const int ch = idx - row * NCH;
-      if (row < valid) {
-        kst[i] = *reinterpret_cast<const bf16x8*>(ksrc + (size_t)row * D + ch * 8);
-        vst[i] = *reinterpret_cast<const bf16x8*>(vsrc + (size_t)row * D + ch * 8);
-      } else {
-        kst[i] = bf16x8{};
-        vst[i] = bf16x8{};
-      }
-    }
-    float bias_v = 0.f;
-    if (kind != 0 && tid < BLK) {
-      if (kind == 1) {
-        bias_v = tid < valid ? 0.f : kNegInf;
-      } else {
-        const int c = (t - n_exact) * BLK + tid;
-        const int n = c < p.C ? cnt_row[c] : 0;
-        bias_v = n > 0 ? fast_log2((float)n) : kNegInf;
-      }
-    }
-    __syncthreads();  // everyone is done reading the previous tile
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = i * THREADS + tid;
-      const int row = idx / NCH;
-      const int ch = idx - row * NCH;
-      *reinterpret_cast<bf16x8*>(k_lds + swz_byte<D>(row, ch)) = kst[i];
-      *reinterpret_cast<bf16x8*>(v_lds + swz_byte<D>(row, ch)) = vst[i];
-    }
-    if (kind != 0 && tid < BLK) bias_lds[tid] = bias_v;
-    __syncthreads();
+    const int st = t & 1;
+    const char* k_lds = smem + 2 * st * TILE;
+    const char* v_lds = k_lds + TILE;
+    const float* bias_lds = bias_base + (2 * st + half) * BLK;
 
-    // S^T tile: rows = keys, columns = this wave's 32 queries.
-    f32x16 sacc[KT];
-#pragma unroll
-    for (int mk = 0; mk < KT; ++mk) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 a = lds_read_b128(k_lds, swz_byte<D>(32 * mk + l32, 2 * s + hl));
-        acc = mfma32x32x16(a, qreg[s], acc);
-      }
-      sacc[mk] = acc;
+    // prefetch tile t+1 into the other stage (free since the barrier closing tile t-1)
+    TileDesc nxt;
+    if (t + 1 < ntiles) {
+      nxt = tile_desc<D, BLK>(p, t + 1, n_list, e0, Kh, Vh, Mh, Bh);
+      char* nk = smem + 2 * (st ^ 1) * TILE;
+      fetch_tile<D, BLK, THREADS>(nxt.k, nxt.valid, nk, tid, w);
+      fetch_tile<D, BLK, THREADS>(nxt.v, nxt.valid, nk + TILE, tid, w);
+      if (nxt.kind != 0 && tid < 2 * BLK) bias_base[2 * (st ^ 1) * BLK + tid] = tile_bias(nxt);
     }
 
-    // Online softmax in the exp2 domain.
-    float mloc = kNegInf;
-    if (kind == 0) {
+    if (block_ok && ((cur.use >> half) & 1)) {
+      // S^T tile: rows = keys, columns = this wave's 32 queries (raw q.k).
+      f32x16 sacc[KT];
 #pragma unroll
-      for (int mk = 0; mk < KT; ++mk)
+      for (int mk = 0; mk < KT; ++mk) {
+        f32x16 acc = f32x16{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = sacc[mk][r] * p.scale_log2e;
-          sacc[mk][r] = x;
-          mloc = fmaxf(mloc, x);
+        for (int s = 0; s < DS; ++s) {
+          const bf16x8 a = lds_read_b128(k_lds, swz_byte<D>(32 * mk + l32, 2 * s + hl));
+          acc = mfma32x32x16(a, qreg[s], acc);
         }
-    } else {
+        sacc[mk] = acc;
+      }
+
+      // Online softmax, log2 domain. Plain exact tiles keep raw scores and fold the scale
+      // into one FMA per element; tiles with a bias row materialise scale*s + bias first.
+      float mt;
+      if (cur.kind == 0) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[mk][r], sacc[mk][r + 1]));
+        mt = fmaxf(mx, xor32(mx)) * c2;
+      } else {
+        float mx = kNegInf;
+#pragma unroll
+        for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 bv =
+                *reinterpret_cast<const f32x4*>(bias_lds + 32 * mk + 8 * i + 4 * hl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x = fmaf(sacc[mk][4 * i + j], c2, bv[j]);
+              sacc[mk][4 * i + j] = x;
+              mx = fmaxf(mx, x);
+            }
+          }
+        mt = fmaxf(mx, xor32(mx));
+      }
+      // Move the reference max only when some row's max outgrows it by > kRescale; until
+      // then probabilities may exceed 1 (at most 2^kRescale), which fp32 and bf16 carry.
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescale) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+      float lsum = 0.f;
+      if (cur.kind == 0) {
+        const float nm = -m_run;
+#pragma unroll
+        for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(sacc[mk][r], c2, nm));
+            sacc[mk][r] = e;
+            lsum += e;
+          }
+      } else {
+#pragma unroll
+        for (int mk = 0; mk < KT; ++mk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(sacc[mk][r] - m_run);
+            sacc[mk][r] = e;
+            lsum += e;
+          }
+      }
+      l_run += lsum;
+
+      // O^T += V^T P^T. k-step (mk, t2) covers keys 32mk + 16t2 + {0..15}; this lane's
+      // eight k-values are keys 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3), which
+      // are exactly its score accumulators 8t2 .. 8t2+7.
 #pragma unroll
       for (int mk = 0; mk < KT; ++mk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_lds + 32 * mk + 8 * i + 4 * hl);
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x8 pb;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = sacc[mk][4 * i + j] * p.scale_log2e + bv[j];
-            sacc[mk][4 * i + j] = x;
-            mloc = fmaxf(mloc, x);
+          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[mk][8 * t2 + e];
+          const int vrow = 32 * mk + 16 * t2 + 4 * (g >> 1) + (gp >> 2);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int col = 32 * dt + 16 * (g & 1) + 4 * (gp & 3);
+            const int cb = ((col & 7) << 1);
+            const bf16x4 lo = lds_read_tr16(v_lds, swz_byte<D>(vrow, col >> 3) + cb);
+            const bf16x4 hi = lds_read_tr16(v_lds, swz_byte<D>(vrow + 8, col >> 3) + cb);
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
           }
         }
     }
-    const float m_new = fmaxf(m_run, fmaxf(mloc, xor32(mloc)));
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
-#pragma unroll
-    for (int mk = 0; mk < KT; ++mk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(sacc[mk][r] - m_new);
-        sacc[mk][r] = e;
-        lsum += e;
-      }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
 
-    // O^T += V^T P^T. k-step (mk, t2) covers keys 32mk + 16t2 + {0..15}; this lane's
-    // eight k-values are keys 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3), which are
-    // exactly its score accumulators 8t2 .. 8t2+7.
-#pragma unroll
-    for (int mk = 0; mk < KT; ++mk)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[mk][8 * t2 + e];
-        const int vrow = 32 * mk + 16 * t2 + 4 * (g >> 1) + (gp >> 2);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int col = 32 * dt + 16 * (g & 1) + 4 * (gp & 3);
-          const int cb = ((col & 7) << 1);
-          const bf16x4 lo = lds_read_tr16(v_lds, swz_byte<D>(vrow, col >> 3) + cb);
-          const bf16x4 hi = lds_read_tr16(v_lds, swz_byte<D>(vrow + 8, col >> 3) + cb);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
-        }
-      }
+    // all waves are done with this stage, and this thread's prefetch has landed
+    __syncthreads();
+    cur = nxt;
   }
 
   // Epilogue: normalise and store. Lane holds O[q][32dt + 8i + 4hl + j].
@@ -410,19 +480,22 @@ fwd_f32_kernel(FwdArgs p) {
 // ----------------------------------------------------------------------------- launch
 template <int D, int BLK>
 static size_t fwd_lds_bytes(bool bf16) {
-  return bf16 ? (size_t)2 * BLK * D * 2 + BLK * 4
+  return bf16 ? (size_t)4 * BLK * D * 2 + 4 * BLK * 4
               : (size_t)BLK * (D + 1) * 4 + (size_t)BLK * (D + 4) * 4 + BLK * 4;
 }
 
 template <int D, int BLK>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool bf16, hipStream_t stream) {
-  const int total = a.H * a.nb;
-  const int grid = ((total + 7) / 8) * 8;
   const size_t lds = fwd_lds_bytes<D, BLK>(bf16);
-  if (bf16)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 2), lds, stream, a);
-  else
+  if (bf16) {
+    const int total = a.H * a.npairs;
+    const int grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 4), lds, stream, a);
+  } else {
+    const int total = a.H * a.nb;
+    const int grid = ((total + 7) / 8) * 8;
     hipLaunchKernelGGL((fwd_f32_kernel<D, BLK>), dim3(grid), dim3(BLK * 2), lds, stream, a);
+  }
   return hipGetLastError();
 }
 

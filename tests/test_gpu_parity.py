@@ -132,12 +132,15 @@ def test_small_bf16_config(lib):
 
 
 # ----------------------------------------------------------------- ragged / edge shapes
-@pytest.mark.parametrize("d,B,dtype", [(128, 128, "bf16"), (64, 128, "bf16"), (128, 64, "bf16"),
-                                       (64, 64, "bf16"), (128, 128, "f32"), (64, 64, "f32")])
-def test_ragged_shapes(lib, d, B, dtype):
-    """N = 1000 (ragged last block), C = 200 (ragged cluster tile), random 30% mask with one
-    empty row and one full row, 2 heads with per-head masks."""
-    H, N, C = 2, 1000, 200
+@pytest.mark.parametrize("d,B,dtype,N", [(128, 128, "bf16", 1000), (128, 128, "bf16", 850),
+                                         (64, 128, "bf16", 850), (128, 64, "bf16", 1000),
+                                         (64, 64, "bf16", 1000), (64, 64, "bf16", 980),
+                                         (128, 128, "f32", 1000), (64, 64, "f32", 1000)])
+def test_ragged_shapes(lib, d, B, dtype, N):
+    """Ragged last block (N = 1000, 980 or 850; 850 and 980 give an odd block count, so the
+    last query-block pair has one block), C = 200 (ragged cluster tile), random 30% mask
+    with one empty row and one full row, 2 heads with per-head masks."""
+    H, C = 2, 200
     L, cache = _random_layer(100 + d + B, H, N, d, dtype, C)
     nb = -(-N // B)
     rng = np.random.default_rng(7)
