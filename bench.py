@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a "
+                         "known-size kernel that calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -249,6 +252,15 @@ def main():
             result["cpu_baseline"] = cpu_baseline(cfg, L2, mask, args.cpu_seconds)
         except Exception as e:  # reported, never fatal to the GPU figure
             result["cpu_baseline"] = {"error": repr(e)}
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
     plan.close()
     print(json.dumps(result), flush=True)
 
