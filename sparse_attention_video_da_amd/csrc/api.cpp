@@ -36,7 +36,6 @@ struct da_plan_s {
   int32_t* d_off = nullptr;
   int32_t* d_start = nullptr;
   int32_t* d_perm = nullptr;
-  void* d_vt = nullptr;          // transposed value tiles for the bf16 forward
   int64_t bytes = 0;
   int device = 0;
 };
@@ -80,8 +79,6 @@ void destroy_device(da_plan_s* p) {
     if (b) (void)hipFree(b);
   p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
   p->d_hist = p->d_off = p->d_start = p->d_perm = nullptr;
-  if (p->d_vt) (void)hipFree(p->d_vt);
-  p->d_vt = nullptr;
 }
 
 std::once_flag g_prep_once;
@@ -180,17 +177,6 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
       return DA_ERR_OUT_OF_MEMORY;
     }
     p->bytes += (int64_t)(a.n * sizeof(int32_t));
-  }
-  if (desc->dtype == DA_DTYPE_BF16) {
-    const size_t nct = (C + desc->block - 1) / desc->block;
-    const size_t vt_bytes = H * (nb + nct) * (size_t)desc->head_dim * desc->block * 2;
-    if (hipMalloc(&p->d_vt, vt_bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      destroy_device(p);
-      delete p;
-      return DA_ERR_OUT_OF_MEMORY;
-    }
-    p->bytes += (int64_t)vt_bytes;
   }
   if (hipMemcpy(p->d_rowptr, p->rowptr.data(), n_rowptr * sizeof(int32_t),
                 hipMemcpyHostToDevice) != hipSuccess ||
@@ -308,8 +294,6 @@ DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void*
   a.prowptr = p->d_prowptr;
   a.pcol = p->d_pcol;
   a.npairs = p->npairs;
-  a.vt = p->d_vt;
-  a.nct = (d.clusters + d.block - 1) / d.block;
   a.O = O;
   a.lse = lse_out;
   a.H = d.heads;

@@ -19,8 +19,6 @@ struct FwdArgs {
   const int32_t* prowptr; // [mask_heads][npairs + 1] lists of query-block pairs (2p, 2p+1)
   const int32_t* pcol;    // union of the pair's exact blocks: kb | (in 2p) << 28 | (in 2p+1) << 29
   int npairs;
-  void* vt;              // workspace: [H][nb + nct][d][BLK] transposed value tiles (bf16)
-  int nct;               // cluster tiles, ceil(C / BLK)
   void* O;
   float* lse;            // may be null
   int H, N, C, nb, mask_heads;
