@@ -124,7 +124,7 @@ def check_reassign_head(K64, V64, mu0_64, mask, block, dtype, gpu: Dict[str, np.
             lim = 1e-5 * np.maximum(rms, 1e-3) + 1e-7
         err = np.abs(g - e)
         assert np.all(err <= lim), f"{what}: {name} off by {float((err / lim).max()):.2f} x tol"
-    return {"band_moves": int(diff.sum()), "keys": int(K64.shape[0])}
+    return {"band_moves": int(diff.sum()), "keys": int(K64.shape[0]), "ref": ref}
 
 
 def oracle_forward_heads(L64: Dict[str, np.ndarray], caches: Dict[int, Dict[str, np.ndarray]],
