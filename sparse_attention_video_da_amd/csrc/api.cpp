@@ -167,7 +167,7 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
   const size_t n_prowptr = p->prowptr.size(), n_pcol = std::max<size_t>(1, p->pcol.size());
   struct Alloc { int32_t** ptr; size_t n; } allocs[] = {
       {&p->d_rowptr, n_rowptr},   {&p->d_col, n_col},   {&p->d_prowptr, n_prowptr},
-      {&p->d_pcol, n_pcol},       {&p->d_hist, H * nb * C}, {&p->d_off, H * nb * C},
+      {&p->d_pcol, n_pcol},       {&p->d_hist, (H * nb * C + 3) / 4}, {&p->d_off, H * nb * C},
       {&p->d_start, H * C},       {&p->d_perm, H * N}};
   for (const Alloc& a : allocs) {
     if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
@@ -255,7 +255,7 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
   a.counts = qblock_counts_out;
   a.rowptr = p->d_rowptr;
   a.col = p->d_col;
-  a.hist = p->d_hist;
+  a.hist = reinterpret_cast<uint8_t*>(p->d_hist);
   a.off = p->d_off;
   a.start = p->d_start;
   a.perm = p->d_perm;

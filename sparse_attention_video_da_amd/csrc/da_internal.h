@@ -36,7 +36,7 @@ struct ReassignArgs {
   int32_t* counts;
   const int32_t* rowptr;
   const int32_t* col;
-  int32_t* hist;   // workspace [H][nb][C]
+  uint8_t* hist;   // workspace [H][nb][C] per-block cluster histograms (<= block keys)
   int32_t* off;    // workspace [H][nb][C]
   int32_t* start;  // workspace [H][C]
   int32_t* perm;   // workspace [H][N]

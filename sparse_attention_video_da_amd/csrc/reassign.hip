@@ -22,19 +22,22 @@ namespace da {
 constexpr float kPosInf = __builtin_inff();
 
 // ----------------------------------------------------------------------------- 1. assign
-// bf16: 4 waves x 32 keys per workgroup. Centroids are staged CH at a time in swizzled
-// LDS together with their squared norms; the score tile D^T = mu * K^T gives each lane one
-// key and 16 centroids per 32-centroid tile, so the argmin stays in registers.
+// bf16: 4 waves x 64 keys per workgroup (2 key tiles of 32 per wave, two waves per SIMD so
+// one wave's argmin VALU work overlaps the other's MFMAs). Centroids are staged CH at a
+// time in swizzled LDS together with their squared norms; the score tile D^T = mu * K^T
+// gives each lane one key and 16 centroids per 32-centroid tile, so the argmin stays in
+// registers, and every centroid operand read from LDS feeds 2 MFMAs.
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mu,
                    int32_t* __restrict__ assign, int N, int C) {
   constexpr int CH = 256;
   constexpr int DS = D / 16;
   constexpr int NCH = D / 8;
   constexpr int PER_T = CH * NCH / 256;
+  constexpr int KTW = 2;           // key tiles (of 32) per wave
   __shared__ __attribute__((aligned(16))) char mu_lds[CH * D * 2];
-  __shared__ float norm_lds[CH];
+  __shared__ __attribute__((aligned(16))) float norm_lds[CH];
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -42,18 +45,27 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
   const int w = tid >> 6;
   const int hl = lane >> 5;
   const int l32 = lane & 31;
-  const int key = blockIdx.x * 128 + w * 32 + l32;
+  const int key0 = blockIdx.x * (4 * 32 * KTW) + w * (32 * KTW) + l32;
   const uint16_t* Kh = K + (size_t)h * N * D;
   const uint16_t* Mh = mu + (size_t)h * C * D;
 
-  bf16x8 kreg[DS];
+  bf16x8 kreg[KTW][DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s)
-    kreg[s] = key < N ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * s + 8 * hl)
-                      : bf16x8{};
+  for (int kt = 0; kt < KTW; ++kt) {
+    const int key = key0 + 32 * kt;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      kreg[kt][s] = key < N ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * s + 8 * hl)
+                            : bf16x8{};
+  }
 
-  float best = kPosInf;
-  int bidx = 0;
+  float best[KTW];
+  int bidx[KTW];
+#pragma unroll
+  for (int kt = 0; kt < KTW; ++kt) {
+    best[kt] = kPosInf;
+    bidx[kt] = 0;
+  }
   for (int c0 = 0; c0 < C; c0 += CH) {
     const int valid = min(CH, C - c0);
     __syncthreads();
@@ -83,33 +95,42 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
     __syncthreads();
     const int ntile = (valid + 31) / 32;
     for (int ct = 0; ct < ntile; ++ct) {
-      f32x16 acc = f32x16{};
+      f32x16 acc[KTW];
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) acc[kt] = f32x16{};
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
         const bf16x8 a = lds_read_b128(mu_lds, swz_byte<D>(32 * ct + l32, 2 * s + hl));
-        acc = mfma32x32x16(a, kreg[s], acc);
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kreg[kt][s], acc[kt]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 nv = *reinterpret_cast<const f32x4*>(norm_lds + 32 * ct + 8 * i + 4 * hl);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float dist = fmaf(-2.f, acc[4 * i + j], nv[j]);
-          if (dist < best) {
-            best = dist;
-            bidx = c0 + 32 * ct + 8 * i + 4 * hl + j;
+          const int c = c0 + 32 * ct + 8 * i + 4 * hl + j;
+#pragma unroll
+          for (int kt = 0; kt < KTW; ++kt) {
+            const float dist = fmaf(-2.f, acc[kt][4 * i + j], nv[j]);
+            if (dist < best[kt]) {   // ascending c per lane: ties keep the lower index
+              best[kt] = dist;
+              bidx[kt] = c;
+            }
           }
         }
       }
     }
   }
-  const float ob = xor32(best);
-  const int oi = __shfl_xor(bidx, 32, 64);
-  if (ob < best || (ob == best && oi < bidx)) {
-    best = ob;
-    bidx = oi;
+#pragma unroll
+  for (int kt = 0; kt < KTW; ++kt) {
+    const float ob = xor32(best[kt]);
+    const int oi = __shfl_xor(bidx[kt], 32, 64);
+    int bi = bidx[kt];
+    if (ob < best[kt] || (ob == best[kt] && oi < bi)) bi = oi;
+    const int key = key0 + 32 * kt;
+    if (hl == 0 && key < N) assign[(size_t)h * N + key] = bi;
   }
-  if (hl == 0 && key < N) assign[(size_t)h * N + key] = bidx;
 }
 
 // fp32: one key per thread, distances in difference form sum (k - mu)^2 in fp32 against
@@ -153,7 +174,7 @@ assign_f32_kernel(const float* __restrict__ K, const float* __restrict__ mu,
 
 // ----------------------------------------------------------------------------- 2. hist
 __global__ void __launch_bounds__(256)
-block_hist_kernel(const int32_t* __restrict__ assign, int32_t* __restrict__ hist, int N, int C,
+block_hist_kernel(const int32_t* __restrict__ assign, uint8_t* __restrict__ hist, int N, int C,
                   int nb, int block) {
   extern __shared__ int32_t hist_lds[];
   const int h = blockIdx.y, kb = blockIdx.x, tid = threadIdx.x;
@@ -162,14 +183,14 @@ block_hist_kernel(const int32_t* __restrict__ assign, int32_t* __restrict__ hist
   const int j = kb * block + tid;
   if (tid < block && j < N) atomicAdd(&hist_lds[assign[(size_t)h * N + j]], 1);
   __syncthreads();
-  int32_t* dst = hist + ((size_t)h * nb + kb) * C;
-  for (int c = tid; c < C; c += 256) dst[c] = hist_lds[c];
+  uint8_t* dst = hist + ((size_t)h * nb + kb) * C;   // a block holds <= 128 keys
+  for (int c = tid; c < C; c += 256) dst[c] = (uint8_t)hist_lds[c];
 }
 
 // ----------------------------------------------------------------------------- 3. col scan
 // 16 waves split the key blocks; lane = cluster. Two passes over the histograms.
 __global__ void __launch_bounds__(1024)
-col_scan_kernel(const int32_t* __restrict__ hist, int32_t* __restrict__ off,
+col_scan_kernel(const uint8_t* __restrict__ hist, int32_t* __restrict__ off,
                 int32_t* __restrict__ sizes, int C, int nb) {
   __shared__ int32_t part[16][64];
   const int h = blockIdx.y;
@@ -177,7 +198,7 @@ col_scan_kernel(const int32_t* __restrict__ hist, int32_t* __restrict__ off,
   const int c = blockIdx.x * 64 + lane;
   const int span = (nb + 15) / 16;
   const int kb0 = min(nb, w * span), kb1 = min(nb, kb0 + span);
-  const int32_t* col = hist + (size_t)h * nb * C + c;
+  const uint8_t* col = hist + (size_t)h * nb * C + c;
   int s = 0;
   if (c < C)
     for (int kb = kb0; kb < kb1; ++kb) s += col[(size_t)kb * C];
@@ -256,7 +277,7 @@ cluster_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
                    const int32_t* __restrict__ start, const int32_t* __restrict__ perm, int N,
                    int C) {
   constexpr int EPL = D / 64;
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int h = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + w;
@@ -336,19 +357,36 @@ cluster_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
 }
 
 // ----------------------------------------------------------------------------- 7. counts
+// n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c]; 4 clusters per thread from
+// the byte histograms (one head's histograms stay resident in L2 across its query blocks).
 __global__ void __launch_bounds__(256)
-counts_kernel(const int32_t* __restrict__ hist, const int32_t* __restrict__ sizes,
+counts_kernel(const uint8_t* __restrict__ hist, const int32_t* __restrict__ sizes,
               const int32_t* __restrict__ rowptr, const int32_t* __restrict__ col,
               int32_t* __restrict__ counts, int C, int nb, int mask_heads) {
   const int h = blockIdx.y, b = blockIdx.x;
   const int mh = mask_heads == 1 ? 0 : h;
   const int e0 = rowptr[mh * (nb + 1) + b], e1 = rowptr[mh * (nb + 1) + b + 1];
-  const int32_t* hh = hist + (size_t)h * nb * C;
+  const uint8_t* hh = hist + (size_t)h * nb * C;
   int32_t* dst = counts + ((size_t)h * nb + b) * C;
-  for (int c = threadIdx.x; c < C; c += 256) {
-    int n = sizes[(size_t)h * C + c];
-    for (int e = e0; e < e1; ++e) n -= hh[(size_t)col[e] * C + c];
-    dst[c] = n;
+  const int32_t* sz = sizes + (size_t)h * C;
+  if ((C & 3) == 0) {
+    for (int c = 4 * threadIdx.x; c < C; c += 4 * 256) {
+      int n0 = sz[c], n1 = sz[c + 1], n2 = sz[c + 2], n3 = sz[c + 3];
+      for (int e = e0; e < e1; ++e) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(hh + (size_t)col[e] * C + c);
+        n0 -= v & 0xff;
+        n1 -= (v >> 8) & 0xff;
+        n2 -= (v >> 16) & 0xff;
+        n3 -= v >> 24;
+      }
+      *reinterpret_cast<int4*>(dst + c) = make_int4(n0, n1, n2, n3);
+    }
+  } else {
+    for (int c = threadIdx.x; c < C; c += 256) {
+      int n = sz[c];
+      for (int e = e0; e < e1; ++e) n -= hh[(size_t)col[e] * C + c];
+      dst[c] = n;
+    }
   }
 }
 
@@ -356,7 +394,7 @@ counts_kernel(const int32_t* __restrict__ hist, const int32_t* __restrict__ size
 template <int D>
 static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL((assign_bf16_kernel<D>), dim3((a.N + 127) / 128, a.H), dim3(256), 0, s,
+    hipLaunchKernelGGL((assign_bf16_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,
                        static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.mu_in),
                        a.assign, a.N, a.C);
   else
