@@ -19,6 +19,8 @@
 namespace da {
 
 constexpr float kNegInf = -__builtin_inff();
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kLn2 = 0.693147180559945309f;
 
 // XCD-aware order: hardware deals workgroup ids round-robin to the 8 XCDs; give each XCD a
@@ -86,8 +88,14 @@ fwd_bf16_kernel(FwdArgs p) {
   constexpr int TILE = BLK * D * 2;
   constexpr int PER_T = (BLK * NCH) / THREADS;   // 16-byte fetches per thread per tensor
   static_assert(PER_T * THREADS == BLK * NCH, "tile must split evenly");
-  constexpr float kRescale = 8.f;  // log2 headroom before the running max is moved
-  constexpr int KC = 2;            // 32-key subtiles per softmax chunk
+  constexpr float kSumLimit = 32768.f;   // partial row sum that forces a max update
+#ifndef FWD_KC
+#define FWD_KC 2
+#endif
+#ifndef FWD_PRIO
+#define FWD_PRIO 1
+#endif
+  constexpr int KC = FWD_KC;       // 32-key subtiles per softmax chunk
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // stage s: K at 2*s*TILE, V at (2*s+1)*TILE; then bias rows [stage][half][BLK]
@@ -199,36 +207,38 @@ fwd_bf16_kernel(FwdArgs p) {
     }
 
     if (block_ok && ((cur.use >> half) & 1)) {
-      // The tile is processed in chunks of KC 32-key subtiles: scores, softmax and the PV
-      // update of one chunk before the next. The lazily moved reference max lets each chunk
-      // use it without seeing the rest of the tile.
+      // The tile is processed in chunks of KC 32-key subtiles. Per chunk: scores (MFMA),
+      // softmax (VALU), PV (MFMA); the scores of chunk c+1 are issued in the same MFMA run
+      // as the PV of chunk c, so each wave alternates one long MFMA run with one VALU run
+      // and the other wave on the SIMD fills the gaps. The lazily moved reference max lets
+      // each chunk use it without seeing the rest of the tile.
+      constexpr int NCK = KT / KC;
+      f32x16 sacc[2][KC];
+      auto qk = [&](int ch, f32x16 (&sc)[KC]) {
 #pragma unroll
-      for (int ch = 0; ch < KT / KC; ++ch) {
-        // S^T chunk: rows = keys, columns = this wave's 32 queries (raw q.k).
-        f32x16 sacc[KC];
+        for (int u = 0; u < KC; ++u) sc[u] = f32x16{};
 #pragma unroll
-        for (int u = 0; u < KC; ++u) {
-          const int mk = ch * KC + u;
-          f32x16 acc = f32x16{};
+        for (int s = 0; s < DS; ++s)
 #pragma unroll
-          for (int s = 0; s < DS; ++s) {
+          for (int u = 0; u < KC; ++u) {
+            const int mk = ch * KC + u;
             const bf16x8 a = lds_read_b128(k_lds, swz_byte<D>(32 * mk + l32, 2 * s + hl));
-            acc = mfma32x32x16(a, qreg[s], acc);
+            sc[u] = mfma32x32x16(a, qreg[s], sc[u]);
           }
-          sacc[u] = acc;
-        }
-        // Plain exact tiles keep raw scores and fold the scale into one FMA per element;
-        // tiles with a bias row materialise scale*s + bias first (log2 domain).
-        float mt;
-        if (cur.kind == 0) {
-          float mx = kNegInf;
+      };
+#if FWD_PRIO
+      __builtin_amdgcn_s_setprio(2);
+#endif
+      qk(0, sacc[0]);
 #pragma unroll
-          for (int u = 0; u < KC; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[u][r], sacc[u][r + 1]));
-          mt = fmaxf(mx, xor32(mx)) * c2;
-        } else {
-          float mx = kNegInf;
+      for (int ch = 0; ch < NCK; ++ch) {
+        f32x16 (&sc)[KC] = sacc[ch & 1];
+#if FWD_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
+        // Tiles with a bias row materialise scale*s + bias (log2 domain); plain exact tiles
+        // keep raw scores and fold the scale into the exponent's FMA.
+        if (cur.kind != 0) {
 #pragma unroll
           for (int u = 0; u < KC; ++u)
 #pragma unroll
@@ -236,17 +246,47 @@ fwd_bf16_kernel(FwdArgs p) {
               const f32x4 bv = *reinterpret_cast<const f32x4*>(
                   bias_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float x = fmaf(sacc[u][4 * i + j], c2, bv[j]);
-                sacc[u][4 * i + j] = x;
-                mx = fmaxf(mx, x);
-              }
+              for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = fmaf(sc[u][4 * i + j], c2, bv[j]);
             }
-          mt = fmaxf(mx, xor32(mx));
         }
-        // Move the reference max only when some row's max outgrows it by > kRescale; until
-        // then probabilities may exceed 1 (at most 2^kRescale), which fp32 and bf16 carry.
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescale) != 0) {
+        const float cs = cur.kind == 0 ? c2 : 1.f;
+        // P = exp2(x - m_run) packed to bf16 (the B operand of O^T += V^T P^T: k-step
+        // (u, t2) covers keys 32mk + 16t2 + {0..15}; this lane's eight k-values are keys
+        // 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3) = score accumulators 8t2 .. 8t2+7).
+        // The row share is summed from the rounded probabilities, two per dot2, so the
+        // denominator sees exactly the weights the numerator does.
+        bf16x8 pk[KC][2];
+        auto exp_pack = [&]() -> float {
+          const float nm = -m_run;
+#pragma unroll
+          for (int u = 0; u < KC; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              pk[u][r >> 3][r & 7] = (__bf16)fast_exp2(fmaf(sc[u][r], cs, nm));
+          float ls = 0.f;
+#pragma unroll
+          for (int u = 0; u < KC; ++u)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+              for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {pk[u][t2][e], pk[u][t2][e + 1]};
+                ls = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, ls, false);
+              }
+          return ls;
+        };
+        float lsum = exp_pack();
+        // The reference max moves only when some row's probabilities outgrow it (a partial
+        // row sum above 2^15, or inf on the first tile); then the chunk's true max is taken,
+        // O and l are rescaled and the chunk is recomputed. Otherwise probabilities may
+        // exceed 1 (each at most 2^15), which fp32 and bf16 carry.
+        if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int u = 0; u < KC; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[u][r], sc[u][r + 1]));
+          const float mt = fmaxf(mx, xor32(mx)) * cs;
           const float m_new = fmaxf(m_run, mt);
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
@@ -255,23 +295,12 @@ fwd_bf16_kernel(FwdArgs p) {
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          lsum = exp_pack();
         }
-        // P (bf16) as the B operand of O^T += V^T P^T: k-step (u, t2) covers keys
-        // 32mk + 16t2 + {0..15}; this lane's eight k-values are keys
-        // 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3) = score accumulators 8t2 .. 8t2+7.
-        bf16x8 pk[KC][2];
-        float lsum = 0.f;
-        const float nm = -m_run;
-        const float cs = cur.kind == 0 ? c2 : 1.f;   // biased scores are already scaled
-#pragma unroll
-        for (int u = 0; u < KC; ++u)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(fmaf(sacc[u][r], cs, nm));
-            lsum += e;
-            pk[u][r >> 3][r & 7] = (__bf16)e;
-          }
         l_run += lsum;
+#if FWD_PRIO
+        __builtin_amdgcn_s_setprio(2);
+#endif
         // V^T operands straight from the row-major V tile by the transposed LDS read: in
         // each 16-lane group, lane 4s + i/4 addresses keys row (s) and 4 dims, and lane i
         // receives those 4 keys for dim i.
@@ -290,7 +319,11 @@ fwd_bf16_kernel(FwdArgs p) {
               oacc[dt] = mfma32x32x16(a, pk[u][t2], oacc[dt]);
             }
           }
+        if (ch + 1 < NCK) qk(ch + 1, sacc[(ch + 1) & 1]);
       }
+#if FWD_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
     }
 
     if (has_next && nxt.kind != 0 && tid < 2 * BLK)

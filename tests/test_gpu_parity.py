@@ -98,8 +98,11 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
         lg.append(lse[h])
         lw.append(ref_lse)
     check_forward(np.concatenate(got_all), np.concatenate(want_all), dtype, f"{what} forward")
-    np.testing.assert_allclose(np.concatenate(lg), np.concatenate(lw), rtol=0,
-                               atol=1e-3 if dtype == "bf16" else 1e-5)
+    # lse tolerance: bf16 probabilities are rounded (RNE) to 8 significant bits before they
+    # are summed into the denominator, so ln l can move by at most ln(1 + 2^-8) < 4e-3
+    lse_err = float(np.max(np.abs(np.concatenate(lg) - np.concatenate(lw))))
+    say(f"  {what} lse: max_abs={lse_err:.3e}")
+    assert lse_err <= (4e-3 if dtype == "bf16" else 1e-5), lse_err
     plan.close()
     return o, caches
 
