@@ -50,6 +50,11 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int byte_off) 
   return *reinterpret_cast<const bf16x8*>(base + byte_off);
 }
 
+// LDS byte address of a shared-memory object (a constant once the kernel's LDS is laid out).
+__device__ __forceinline__ int lds_addr(const void* p) {
+  return (int)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // gfx950 transposed LDS read: within each 16-lane group, output lane i, slot s receives
 // element (i % 4) of the 8 bytes addressed by lane 4*s + i/4 of the same group.
 __device__ __forceinline__ bf16x4 lds_read_tr16(const char* base, int byte_off) {

@@ -19,9 +19,9 @@
 namespace da {
 
 constexpr float kNegInf = -__builtin_inff();
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kLn2 = 0.693147180559945309f;
+// Word 3 of a gfx9-family raw buffer resource (32-bit data format, no swizzle or stride).
+constexpr int kBufferWord3 = 0x00020000;
 
 // XCD-aware order: hardware deals workgroup ids round-robin to the 8 XCDs; give each XCD a
 // contiguous range of (head, query block) so neighbouring query blocks, which share many
@@ -38,8 +38,7 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
 // their key blocks), then the cluster tiles, which both blocks use with their own bias
 // rows. A wave skips the tiles its block does not keep.
 struct TileDesc {
-  const char* k;   // tile base (bytes)
-  const char* v;
+  int off;         // byte offset of the tile's first row in K and V, or in the cache arrays
   int valid;       // rows that exist (keys < N, or clusters < C)
   int kind;        // 0 full exact block, 1 ragged exact block, 2 cluster tile
   int c0;          // first cluster of a cluster tile
@@ -52,14 +51,11 @@ __device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
 }
 
 template <int D, int BLK>
-__device__ __forceinline__ TileDesc tile_desc(int t, int n_list, int entry, int N, int C,
-                                              const char* Kh, const char* Vh, const char* Mh,
-                                              const char* Bh) {
+__device__ __forceinline__ TileDesc tile_desc(int t, int n_list, int entry, int N, int C) {
   TileDesc d;
   if (t < n_list) {
     const int kb = entry & 0x0fffffff;
-    d.k = Kh + (size_t)kb * BLK * D * 2;
-    d.v = Vh + (size_t)kb * BLK * D * 2;
+    d.off = kb * BLK * D * 2;
     d.valid = min(BLK, N - kb * BLK);
     d.kind = d.valid < BLK ? 1 : 0;
     d.c0 = 0;
@@ -67,13 +63,26 @@ __device__ __forceinline__ TileDesc tile_desc(int t, int n_list, int entry, int 
   } else {
     const int ct = t - n_list;
     d.c0 = ct * BLK;
-    d.k = Mh + (size_t)d.c0 * D * 2;
-    d.v = Bh + (size_t)d.c0 * D * 2;
+    d.off = d.c0 * D * 2;
     d.valid = min(BLK, C - d.c0);
     d.kind = 2;
     d.use = 3;
   }
   return d;
+}
+
+// Scheduling groups for one software-pipelined chunk: NPRE LDS reads, then G times {one
+// MFMA, ND LDS reads, NV VALU instructions}, so the matrix core and the VALU of one wave
+// run side by side and the operand reads run ahead of the MFMAs that consume them.
+template <int G, int NV, int ND, int NPRE>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  if constexpr (NPRE > 0) __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (ND > 0) __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
 }
 
 template <int D, int BLK>
@@ -92,14 +101,27 @@ fwd_bf16_kernel(FwdArgs p) {
 #ifndef FWD_KC
 #define FWD_KC 2
 #endif
-#ifndef FWD_PRIO
-#define FWD_PRIO 1
+#ifndef FWD_NV
+#define FWD_NV 7
+#endif
+#ifndef FWD_ND
+#define FWD_ND 0
+#endif
+#ifndef FWD_NPRE
+#define FWD_NPRE 0
 #endif
   constexpr int KC = FWD_KC;       // 32-key subtiles per softmax chunk
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  // stage s: K at 2*s*TILE, V at (2*s+1)*TILE; then bias rows [stage][half][BLK]
-  float* bias_base = reinterpret_cast<float*>(smem + 4 * TILE);
+  // Two LDS stages, each stage's K and V tiles a separate object: with the stage chosen
+  // statically (the tile loop is unrolled by two) the compiler can tell that the transposed
+  // reads of one stage never alias the direct-to-LDS prefetch into the other, and it does
+  // not drain the prefetch before them.
+  __shared__ __attribute__((aligned(256))) char k_s0[TILE];
+  __shared__ __attribute__((aligned(256))) char k_s1[TILE];
+  __shared__ __attribute__((aligned(256))) char v_s0[TILE];
+  __shared__ __attribute__((aligned(256))) char v_s1[TILE];
+  __shared__ __attribute__((aligned(16))) float bias_s0[2 * BLK];   // [half][BLK]
+  __shared__ __attribute__((aligned(16))) float bias_s1[2 * BLK];
 
   const int total = p.H * p.npairs;
   const int logical = xcd_remap(blockIdx.x, total);
@@ -134,18 +156,25 @@ fwd_bf16_kernel(FwdArgs p) {
   // Direct-to-LDS fetch of one K or V tile: the lane filling physical LDS slot (row, pc)
   // reads logical chunk pc ^ swz_key(row); each wave instruction fills 1 KB of consecutive
   // slots. Rows past `valid` re-read the last valid row: their logits are masked to -inf
-  // (and their probabilities are 0), so their contents only need to be finite.
-  auto fetch = [&](const char* src, int valid, char* lds_tile) {
+  // (and their probabilities are 0), so their contents only need to be finite. The loads go
+  // through buffer resources (one per head and tensor, bounded by the tensor's size): unlike
+  // the global form they are not flat instructions, so while they are in flight the LDS
+  // reads of the current tile keep fine-grained waits.
+  auto rsrc = [](const char* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t rK = rsrc(Kh, p.N * D * 2), rV = rsrc(Vh, p.N * D * 2);
+  const __amdgpu_buffer_rsrc_t rM = rsrc(Mh, p.C * D * 2), rB = rsrc(Bh, p.C * D * 2);
+  auto fetch = [&](__amdgpu_buffer_rsrc_t r, int base, int valid, char* lds_tile) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int slot = i * THREADS + tid;
       const int row = slot / NCH;
       const int pc = slot - row * NCH;
-      const int off = min(row, valid - 1) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src + off),
-          (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16),
-          16, 0, 0);
+      const int off = base + min(row, valid - 1) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16),
+          16, off, 0, 0, 0);
     }
   };
   // Bias rows (log2 domain): thread tid < 2*BLK owns [tid / BLK][tid % BLK]: 0 / -inf past
@@ -157,17 +186,20 @@ fwd_bf16_kernel(FwdArgs p) {
     const int c = d.c0 + brow;
     return (d.kind == 2 && tid < 2 * BLK && c < p.C && bq < p.nb) ? cnt_row[c] : 0;
   };
+  // Stored divided by the log2-domain scale: the score accumulators start from it, so the
+  // softmax of every tile kind is exp2(scale * (b / scale + q.k) - m).
+  const float inv_c2 = 1.f / p.scale_log2e;
   auto bias_of = [&](const TileDesc& d, int n) -> float {
+    if (d.kind == 0) return 0.f;
     if (d.kind == 1) return brow < d.valid ? 0.f : kNegInf;
-    return n > 0 ? fast_log2((float)n) : kNegInf;
+    return n > 0 ? fast_log2((float)n) * inv_c2 : kNegInf;
   };
 
   // prologue: tile 0 into stage 0
-  TileDesc cur = tile_desc<D, BLK>(0, n_list, n_list > 0 ? sload(p.pcol, e0) : 0, p.N, p.C,
-                                   Kh, Vh, Mh, Bh);
-  fetch(cur.k, cur.valid, smem);
-  fetch(cur.v, cur.valid, smem + TILE);
-  if (cur.kind != 0 && tid < 2 * BLK) bias_base[tid] = bias_of(cur, load_count(cur));
+  TileDesc cur = tile_desc<D, BLK>(0, n_list, n_list > 0 ? sload(p.pcol, e0) : 0, p.N, p.C);
+  fetch(cur.kind == 2 ? rM : rK, cur.off, cur.valid, k_s0);
+  fetch(cur.kind == 2 ? rB : rV, cur.off, cur.valid, v_s0);
+  if (tid < 2 * BLK) bias_s0[tid] = bias_of(cur, load_count(cur));
   int ent_next = n_list > 1 ? sload(p.pcol, e0 + 1) : 0;
 
   // Q^T operand for this lane's query, all d k-steps.
@@ -181,6 +213,16 @@ fwd_bf16_kernel(FwdArgs p) {
       qreg[s] = bf16x8{};
   }
 
+  // Lane parts of the swizzled LDS read addresses. The swizzle key of a row depends only on
+  // its low four bits, so across the reads of a tile the K address is
+  // kx ^ (s << 5) + 32 mk rows and the V address vx ^ (dt << 6) + rows: one base per operand
+  // class, the XOR touching bits below 256 and the rest an immediate offset.
+  const int kx = l32 * (2 * D) + ((hl ^ swz_key<D>(l32)) << 4);
+  const int vr = 4 * (g >> 1) + (gp >> 2);
+  const int vc = 2 * (g & 1) + ((gp & 3) >> 1);
+  const int vx_lo = vr * (2 * D) + ((vc ^ swz_key<D>(vr)) << 4) + ((gp & 1) << 3);
+  const int vx_hi = (vr + 8) * (2 * D) + ((vc ^ swz_key<D>(vr + 8)) << 4) + ((gp & 1) << 3);
+
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
@@ -189,104 +231,116 @@ fwd_bf16_kernel(FwdArgs p) {
   const float c2 = p.scale_log2e;
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    const char* k_lds = smem + 2 * st * TILE;
-    const char* v_lds = k_lds + TILE;
-    const float* bias_lds = bias_base + (2 * st + half) * BLK;
+  // one tile: compute on (k_lds, v_lds, bias_cur) while tile t+1 streams into (nk, nv)
+  auto tile = [&](int t, const char* k_lds, const char* v_lds, const float* bias_cur,
+                  char* nk, char* nv, float* bias_nxt) {
+    const float* bias_lds = bias_cur + half * BLK;
 
     // prefetch tile t+1 into the other stage (free since the barrier closing tile t-1)
     const bool has_next = t + 1 < ntiles;
-    const TileDesc nxt = tile_desc<D, BLK>(t + 1, n_list, ent_next, p.N, p.C, Kh, Vh, Mh, Bh);
+    const TileDesc nxt = tile_desc<D, BLK>(t + 1, n_list, ent_next, p.N, p.C);
     int cnt_next = 0;
     if (has_next) {
-      char* nk = smem + 2 * (st ^ 1) * TILE;
-      fetch(nxt.k, nxt.valid, nk);
-      fetch(nxt.v, nxt.valid, nk + TILE);
+      fetch(nxt.kind == 2 ? rM : rK, nxt.off, nxt.valid, nk);
+      fetch(nxt.kind == 2 ? rB : rV, nxt.off, nxt.valid, nv);
       cnt_next = load_count(nxt);
     }
 
     if (block_ok && ((cur.use >> half) & 1)) {
-      // The tile is processed in chunks of KC 32-key subtiles. Per chunk: scores (MFMA),
-      // softmax (VALU), PV (MFMA); the scores of chunk c+1 are issued in the same MFMA run
-      // as the PV of chunk c, so each wave alternates one long MFMA run with one VALU run
-      // and the other wave on the SIMD fills the gaps. The lazily moved reference max lets
-      // each chunk use it without seeing the rest of the tile.
+      // This stage's read bases as LDS byte addresses, opaque per tile so that the compiler
+      // keeps one set live (not both stages' hoisted copies) and folds the row offsets
+      // into the reads' immediate field. The tiles are 256-byte aligned, so adding the
+      // tile address commutes with the XORs.
+      const int ka = lds_addr(k_lds), va = lds_addr(v_lds);
+      int kb = kx + ka, vlo = vx_lo + va, vhi = vx_hi + va;
+      asm volatile("" : "+v"(kb), "+v"(vlo), "+v"(vhi));
+      // The tile is processed in chunks of KC 32-key subtiles, software-pipelined inside
+      // each wave: while the VALU computes the softmax of chunk c, the matrix core runs the
+      // scores of chunk c+1 and the PV product of chunk c-1 (both independent of it), the
+      // two instruction streams interleaved by the scheduling groups below. The lazily
+      // moved reference max lets each chunk use it without seeing the rest of the tile.
       constexpr int NCK = KT / KC;
       f32x16 sacc[2][KC];
+      // P = exp2(x - m_run) packed to bf16 (the B operand of O^T += V^T P^T: k-step
+      // (u, t2) covers keys 32mk + 16t2 + {0..15}; this lane's eight k-values are keys
+      // 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3) = score accumulators 8t2 .. 8t2+7).
+      bf16x8 pk[2][KC][2];
+      // Scores start from the tile's bias row (0 for a full exact block, -inf past N, and
+      // log2 of the outside count for a cluster tile, all divided by the scale).
       auto qk = [&](int ch, f32x16 (&sc)[KC]) {
 #pragma unroll
-        for (int u = 0; u < KC; ++u) sc[u] = f32x16{};
+        for (int u = 0; u < KC; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(
+                bias_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = bv[j];
+          }
 #pragma unroll
         for (int s = 0; s < DS; ++s)
 #pragma unroll
           for (int u = 0; u < KC; ++u) {
             const int mk = ch * KC + u;
-            const bf16x8 a = lds_read_b128(k_lds, swz_byte<D>(32 * mk + l32, 2 * s + hl));
+            const bf16x8 a = lds_read_b128(k_lds, (kb ^ (s << 5)) - ka + mk * 64 * D);
             sc[u] = mfma32x32x16(a, qreg[s], sc[u]);
           }
       };
-#if FWD_PRIO
-      __builtin_amdgcn_s_setprio(2);
-#endif
+      // V^T operands straight from the row-major V tile by the transposed LDS read: in
+      // each 16-lane group, lane 4s + i/4 addresses keys row (s) and 4 dims, and lane i
+      // receives those 4 keys for dim i.
+      auto pv = [&](int ch, const bf16x8 (&pc)[KC][2]) {
+#pragma unroll
+        for (int u = 0; u < KC; ++u)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const int roff = (32 * (ch * KC + u) + 16 * t2) * (2 * D) - va;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const bf16x4 lo = lds_read_tr16(v_lds, (vlo ^ (dt << 6)) + roff);
+              const bf16x4 hi = lds_read_tr16(v_lds, (vhi ^ (dt << 6)) + roff);
+              const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              oacc[dt] = mfma32x32x16(a, pc[u][t2], oacc[dt]);
+            }
+          }
+      };
+      // The row share is summed in fp32 from the unrounded probabilities (plain adds, which
+      // run beside the MFMAs; the packed dot product does not), four partial sums deep.
+      auto exp_pack = [&](const f32x16 (&sc)[KC], bf16x8 (&pc)[KC][2]) -> float {
+        const float nm = -m_run;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KC; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(sc[u][r], c2, nm));
+            pc[u][r >> 3][r & 7] = (__bf16)e;
+            ls[r & 3] += e;
+          }
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
       qk(0, sacc[0]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ch = 0; ch < NCK; ++ch) {
         f32x16 (&sc)[KC] = sacc[ch & 1];
-#if FWD_PRIO
-        __builtin_amdgcn_s_setprio(0);
-#endif
-        // Tiles with a bias row materialise scale*s + bias (log2 domain); plain exact tiles
-        // keep raw scores and fold the scale into the exponent's FMA.
-        if (cur.kind != 0) {
-#pragma unroll
-          for (int u = 0; u < KC; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const f32x4 bv = *reinterpret_cast<const f32x4*>(
-                  bias_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = fmaf(sc[u][4 * i + j], c2, bv[j]);
-            }
-        }
-        const float cs = cur.kind == 0 ? c2 : 1.f;
-        // P = exp2(x - m_run) packed to bf16 (the B operand of O^T += V^T P^T: k-step
-        // (u, t2) covers keys 32mk + 16t2 + {0..15}; this lane's eight k-values are keys
-        // 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3) = score accumulators 8t2 .. 8t2+7).
-        // The row share is summed from the rounded probabilities, two per dot2, so the
-        // denominator sees exactly the weights the numerator does.
-        bf16x8 pk[KC][2];
-        auto exp_pack = [&]() -> float {
-          const float nm = -m_run;
-#pragma unroll
-          for (int u = 0; u < KC; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              pk[u][r >> 3][r & 7] = (__bf16)fast_exp2(fmaf(sc[u][r], cs, nm));
-          float ls = 0.f;
-#pragma unroll
-          for (int u = 0; u < KC; ++u)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-              for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {pk[u][t2][e], pk[u][t2][e + 1]};
-                ls = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, ls, false);
-              }
-          return ls;
-        };
-        float lsum = exp_pack();
+        bf16x8 (&pc)[KC][2] = pk[ch & 1];
+        if (ch + 1 < NCK) qk(ch + 1, sacc[(ch + 1) & 1]);
+        if (ch > 0) pv(ch - 1, pk[(ch - 1) & 1]);
+        float lsum = exp_pack(sc, pc);
+        interleave_mfma_valu<16 * KC, FWD_NV, FWD_ND, FWD_NPRE>();
         // The reference max moves only when some row's probabilities outgrow it (a partial
         // row sum above 2^15, or inf on the first tile); then the chunk's true max is taken,
-        // O and l are rescaled and the chunk is recomputed. Otherwise probabilities may
-        // exceed 1 (each at most 2^15), which fp32 and bf16 carry.
+        // O (including the PV of chunk c-1, computed at the old max) and l are rescaled and
+        // the chunk is recomputed. Otherwise probabilities may exceed 1 (each at most
+        // 2^15), which fp32 and bf16 carry.
         if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) {
           float mx = kNegInf;
 #pragma unroll
           for (int u = 0; u < KC; ++u)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[u][r], sc[u][r + 1]));
-          const float mt = fmaxf(mx, xor32(mx)) * cs;
+          const float mt = fmaxf(mx, xor32(mx)) * c2;
           const float m_new = fmaxf(m_run, mt);
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
@@ -295,45 +349,24 @@ fwd_bf16_kernel(FwdArgs p) {
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-          lsum = exp_pack();
+          lsum = exp_pack(sc, pc);
         }
         l_run += lsum;
-#if FWD_PRIO
-        __builtin_amdgcn_s_setprio(2);
-#endif
-        // V^T operands straight from the row-major V tile by the transposed LDS read: in
-        // each 16-lane group, lane 4s + i/4 addresses keys row (s) and 4 dims, and lane i
-        // receives those 4 keys for dim i.
-#pragma unroll
-        for (int u = 0; u < KC; ++u)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            const int vrow = 32 * (ch * KC + u) + 16 * t2 + 4 * (g >> 1) + (gp >> 2);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              const int col = 32 * dt + 16 * (g & 1) + 4 * (gp & 3);
-              const int cb = ((col & 7) << 1);
-              const bf16x4 lo = lds_read_tr16(v_lds, swz_byte<D>(vrow, col >> 3) + cb);
-              const bf16x4 hi = lds_read_tr16(v_lds, swz_byte<D>(vrow + 8, col >> 3) + cb);
-              const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              oacc[dt] = mfma32x32x16(a, pk[u][t2], oacc[dt]);
-            }
-          }
-        if (ch + 1 < NCK) qk(ch + 1, sacc[(ch + 1) & 1]);
       }
-#if FWD_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
+      pv(NCK - 1, pk[(NCK - 1) & 1]);
     }
 
-    if (has_next && nxt.kind != 0 && tid < 2 * BLK)
-      bias_base[2 * (st ^ 1) * BLK + tid] = bias_of(nxt, cnt_next);
+    if (has_next && tid < 2 * BLK) bias_nxt[tid] = bias_of(nxt, cnt_next);
     // list entry of tile t+2, read here so no scalar load is in flight during the compute
     // (an outstanding scalar load forces every LDS wait to drain completely)
     ent_next = t + 2 < n_list ? sload(p.pcol, e0 + t + 2) : 0;
     // all waves are done with this stage, and this thread's prefetch has landed
     __syncthreads();
     cur = nxt;
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, k_s0, v_s0, bias_s0, k_s1, v_s1, bias_s1);
+    if (t + 1 < ntiles) tile(t + 1, k_s1, v_s1, bias_s1, k_s0, v_s0, bias_s0);
   }
 
   // Epilogue: normalise and store. Lane holds O[q][32dt + 8i + 4hl + j].
@@ -532,7 +565,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, bool bf16, hipStream_t stream) 
   if (bf16) {
     const int total = a.H * a.npairs;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 4), lds, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 4), 0, stream, a);
   } else {
     const int total = a.H * a.nb;
     const int grid = ((total + 7) / 8) * 8;
@@ -552,10 +585,6 @@ hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, bool bf16,
 
 template <int D, int BLK>
 static hipError_t prep_fwd() {
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fwd_bf16_kernel<D, BLK>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)fwd_lds_bytes<D, BLK>(true));
-  if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32_kernel<D, BLK>),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)fwd_lds_bytes<D, BLK>(false));
