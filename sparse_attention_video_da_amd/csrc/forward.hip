@@ -132,7 +132,7 @@ fwd_bf16_kernel(FwdArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept scalar
   const int half = w / WPB;
   const int wq = w - half * WPB;
   const int hl = lane >> 5;
@@ -165,16 +165,31 @@ fwd_bf16_kernel(FwdArgs p) {
   };
   const __amdgpu_buffer_rsrc_t rK = rsrc(Kh, p.N * D * 2), rV = rsrc(Vh, p.N * D * 2);
   const __amdgpu_buffer_rsrc_t rM = rsrc(Mh, p.C * D * 2), rB = rsrc(Bh, p.C * D * 2);
+  // Pass i of a full tile covers rows ROWS_I*i + tid/NCH; ROWS_I is a multiple of 16, so the
+  // swizzle key, and with it the whole per-lane offset, is the same in every pass: the lane
+  // offset is computed once and each pass only moves the scalar tile offset. Ragged tiles
+  // (the last key block, a short last cluster tile) clamp their rows on the slow path.
+  constexpr int ROWS_I = THREADS / NCH;
+  static_assert(ROWS_I % 16 == 0, "swizzle key must repeat across fetch passes");
+  const int f_off0 = (tid / NCH) * (D * 2) + (((tid % NCH) ^ swz_key<D>(tid / NCH)) << 4);
   auto fetch = [&](__amdgpu_buffer_rsrc_t r, int base, int valid, char* lds_tile) {
+    if (valid == BLK) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int slot = i * THREADS + tid;
-      const int row = slot / NCH;
-      const int pc = slot - row * NCH;
-      const int off = base + min(row, valid - 1) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16),
-          16, off, 0, 0, 0);
+      for (int i = 0; i < PER_T; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16),
+            16, f_off0, base + i * ROWS_I * D * 2, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        const int slot = i * THREADS + tid;
+        const int row = slot / NCH;
+        const int pc = slot - row * NCH;
+        const int off = base + min(row, valid - 1) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16),
+            16, off, 0, 0, 0);
+      }
     }
   };
   // Bias rows (log2 domain): thread tid < 2*BLK owns [tid / BLK][tid % BLK]: 0 / -inf past
