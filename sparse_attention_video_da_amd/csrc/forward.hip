@@ -102,13 +102,16 @@ fwd_bf16_kernel(FwdArgs p) {
 #define FWD_KC 2
 #endif
 #ifndef FWD_NV
-#define FWD_NV 7
+#define FWD_NV 5
 #endif
 #ifndef FWD_ND
-#define FWD_ND 0
+#define FWD_ND 2
 #endif
 #ifndef FWD_NPRE
-#define FWD_NPRE 0
+#define FWD_NPRE 8
+#endif
+#ifndef FWD_Q0PRE
+#define FWD_Q0PRE 12
 #endif
   constexpr int KC = FWD_KC;       // 32-key subtiles per softmax chunk
 
@@ -335,6 +338,14 @@ fwd_bf16_kernel(FwdArgs p) {
         return (ls[0] + ls[1]) + (ls[2] + ls[3]);
       };
       qk(0, sacc[0]);
+      // the first chunk's scores have no softmax to hide behind: issue their operand reads
+      // well ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, FWD_Q0PRE, 0);
+#pragma unroll
+      for (int i = 0; i < DS * KC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ch = 0; ch < NCK; ++ch) {
