@@ -36,6 +36,7 @@ struct da_plan_s {
   int32_t* d_off = nullptr;
   int32_t* d_start = nullptr;
   int32_t* d_perm = nullptr;
+  int32_t* d_cop = nullptr;
   int64_t bytes = 0;
   int device = 0;
 };
@@ -74,11 +75,11 @@ da_status check_desc(const da_desc* d) {
 
 void destroy_device(da_plan_s* p) {
   int32_t* bufs[] = {p->d_rowptr, p->d_col,   p->d_prowptr, p->d_pcol,
-                     p->d_hist,   p->d_off,   p->d_start,   p->d_perm};
+                     p->d_hist,   p->d_off,   p->d_start,   p->d_perm, p->d_cop};
   for (int32_t* b : bufs)
     if (b) (void)hipFree(b);
   p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
-  p->d_hist = p->d_off = p->d_start = p->d_perm = nullptr;
+  p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = nullptr;
 }
 
 std::once_flag g_prep_once;
@@ -168,7 +169,8 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
   struct Alloc { int32_t** ptr; size_t n; } allocs[] = {
       {&p->d_rowptr, n_rowptr},   {&p->d_col, n_col},   {&p->d_prowptr, n_prowptr},
       {&p->d_pcol, n_pcol},       {&p->d_hist, (H * nb * C + 3) / 4}, {&p->d_off, H * nb * C},
-      {&p->d_start, H * C},       {&p->d_perm, H * N}};
+      {&p->d_start, H * C},       {&p->d_perm, H * N},
+      {&p->d_cop, (H * C * ((size_t)desc->head_dim + 8) * 2 + 3) / 4}};
   for (const Alloc& a : allocs) {
     if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -259,6 +261,7 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
   a.off = p->d_off;
   a.start = p->d_start;
   a.perm = p->d_perm;
+  a.cop = reinterpret_cast<uint16_t*>(p->d_cop);
   a.H = d.heads;
   a.N = d.seq_len;
   a.C = d.clusters;

@@ -50,6 +50,9 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int byte_off) 
   return *reinterpret_cast<const bf16x8*>(base + byte_off);
 }
 
+// Word 3 of a gfx9-family raw buffer resource (32-bit data format, no swizzle or stride).
+constexpr int kBufferWord3 = 0x00020000;
+
 // LDS byte address of a shared-memory object (a constant once the kernel's LDS is laid out).
 __device__ __forceinline__ int lds_addr(const void* p) {
   return (int)(uintptr_t)(const __attribute__((address_space(3))) char*)p;

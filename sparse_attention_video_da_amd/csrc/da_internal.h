@@ -40,6 +40,7 @@ struct ReassignArgs {
   int32_t* off;    // workspace [H][nb][C]
   int32_t* start;  // workspace [H][C]
   int32_t* perm;   // workspace [H][N]
+  uint16_t* cop;   // workspace: bf16 distance operands, [H][C][D] (-2 mu) then [H][C][8]
   int H, N, C, nb, block, mask_heads;
 };
 

@@ -20,8 +20,6 @@ namespace da {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
-// Word 3 of a gfx9-family raw buffer resource (32-bit data format, no swizzle or stride).
-constexpr int kBufferWord3 = 0x00020000;
 
 // XCD-aware order: hardware deals workgroup ids round-robin to the 8 XCDs; give each XCD a
 // contiguous range of (head, query block) so neighbouring query blocks, which share many

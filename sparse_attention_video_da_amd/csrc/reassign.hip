@@ -20,114 +20,263 @@
 namespace da {
 
 constexpr float kPosInf = __builtin_inff();
+#ifndef ASG_PRE
+#define ASG_PRE 4
+#endif
+#ifndef ASG_WAVES
+#define ASG_WAVES 4
+#endif
+#ifndef ASG_CH
+#define ASG_CH 128
+#endif
 
 // ----------------------------------------------------------------------------- 1. assign
-// bf16: 4 waves x 64 keys per workgroup (2 key tiles of 32 per wave, two waves per SIMD so
-// one wave's argmin VALU work overlaps the other's MFMAs). Centroids are staged CH at a
-// time in swizzled LDS together with their squared norms; the score tile D^T = mu * K^T
-// gives each lane one key and 16 centroids per 32-centroid tile, so the argmin stays in
-// registers, and every centroid operand read from LDS feeds 2 MFMAs.
+// bf16 distances come straight out of the MFMA. Per centroid, a pre-pass writes the product
+// operands: -2 mu (exact in bf16) and an 8-element row [h, m, l, 1, 1, 1, 0, 0] whose three
+// bf16 parts h + m + l carry |mu|^2 (fp32, about 24 bits). Each key gets the matching row
+// [1, 1, 1, h', m', l', 0, 0] for |k|^2, so one extra 16-deep MFMA step (of D/16 + 1) leaves
+// the squared distance |k|^2 + |mu|^2 - 2 k.mu in the accumulator.
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mu,
-                   int32_t* __restrict__ assign, int N, int C) {
-  constexpr int CH = 256;
+__global__ void __launch_bounds__(256)
+centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__ mup,
+                         uint16_t* __restrict__ aug, int C) {
+  const int h = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  const size_t row = (size_t)h * C + c;
+  const uint16_t* src = mu + row * D;
+  uint16_t* dst = mup + row * D;
+  float nrm = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < D / 8; ++ch) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * ch);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = bf16_to_f32((uint16_t)(wv[q] & 0xffffu));
+      const float hi = bf16_to_f32((uint16_t)(wv[q] >> 16));
+      nrm = fmaf(lo, lo, nrm);
+      nrm = fmaf(hi, hi, nrm);
+      // -2x is exact in bf16 (finite inputs): flip the sign, double through fp32
+      o[q] = (uint32_t)f32_to_bf16_rne(-2.f * lo) | ((uint32_t)f32_to_bf16_rne(-2.f * hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + 8 * ch) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  const uint16_t n0 = f32_to_bf16_rne(nrm);
+  const float r1 = nrm - bf16_to_f32(n0);
+  const uint16_t n1 = f32_to_bf16_rne(r1);
+  const uint16_t n2 = f32_to_bf16_rne(r1 - bf16_to_f32(n1));
+  constexpr uint16_t kOne = 0x3f80;
+  *reinterpret_cast<uint4*>(aug + row * 8) =
+      make_uint4((uint32_t)n0 | ((uint32_t)n1 << 16), (uint32_t)n2 | ((uint32_t)kOne << 16),
+                 (uint32_t)kOne | ((uint32_t)kOne << 16), 0u);
+}
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | ((n >> 4) << 14); }
+
+// 8 waves x 64 keys per workgroup (2 key tiles of 32 per wave). Centroid chunks of CH are
+// staged in swizzled LDS by direct buffer loads, two chunks at a time. The score tile
+// D^T = mu * K^T gives each lane one key and 16 centroids per 32-centroid tile; the lane
+// packs a 5-bit tile-local index into the low mantissa bits of each distance (a change
+// below 2^-18 relative, far inside the 1e-4 tie band) and keeps the integer minimum with
+// three-way mins. Distances are non-negative up to rounding; a slightly negative one (a key
+// equal to a centroid) orders below every positive one as an integer, which is the right
+// winner.
+template <int D, int WAVES, int CH>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
+                   const uint16_t* __restrict__ aug, int32_t* __restrict__ assign, int N,
+                   int C) {
   constexpr int DS = D / 16;
   constexpr int NCH = D / 8;
-  constexpr int PER_T = CH * NCH / 256;
-  constexpr int KTW = 2;           // key tiles (of 32) per wave
-  __shared__ __attribute__((aligned(16))) char mu_lds[CH * D * 2];
-  __shared__ __attribute__((aligned(16))) float norm_lds[CH];
+  constexpr int THREADS = WAVES * 64;
+  constexpr int KTW = 2;
+  constexpr int KEYS = (THREADS / 64) * 32 * KTW;
+  constexpr int PER_T = CH * NCH / THREADS;
+  static_assert(PER_T * THREADS == CH * NCH, "chunk must split evenly");
+  __shared__ __attribute__((aligned(256))) char mu_s0[CH * D * 2];
+  __shared__ __attribute__((aligned(256))) char mu_s1[CH * D * 2];
+  __shared__ __attribute__((aligned(16))) char aug_s0[CH * 16];
+  __shared__ __attribute__((aligned(16))) char aug_s1[CH * 16];
 
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;
   const int l32 = lane & 31;
-  const int key0 = blockIdx.x * (4 * 32 * KTW) + w * (32 * KTW) + l32;
+  const int key0 = blockIdx.x * KEYS + w * (32 * KTW) + l32;
   const uint16_t* Kh = K + (size_t)h * N * D;
-  const uint16_t* Mh = mu + (size_t)h * C * D;
+  const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(mup + (size_t)h * C * D), (short)0, C * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(aug + (size_t)h * C * 8), (short)0, C * 16, kBufferWord3);
+  const int nchunks = (C + CH - 1) / CH;
 
+  // Stage chunk ci: rows past the chunk's valid count re-read its last row (their
+  // distances are masked below).
+  auto stage = [&](int ci, char* ms, char* as) {
+    const int c0 = ci * CH;
+    const int valid = min(CH, C - c0);
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int slot = i * THREADS + tid;
+      const int row = slot / NCH;
+      const int pc = slot - row * NCH;
+      const int off = (c0 + min(row, valid - 1)) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rM, (__attribute__((address_space(3))) void*)(ms + (i * THREADS + w * 64) * 16), 16,
+          off, 0, 0, 0);
+    }
+    if (tid < CH)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (__attribute__((address_space(3))) void*)(as + w * 64 * 16), 16,
+          (c0 + min(tid, valid - 1)) * 16, 0, 0, 0);
+  };
+
+  // This lane's keys: the B operand of D^T = mu K^T (dims 16s + 8hl .. +7), and the
+  // augmented row for |k|^2 on the lower half (zero on the upper half, so whatever the
+  // centroid side holds in dims 8..15 of that step contributes nothing).
   bf16x8 kreg[KTW][DS];
+  bf16x8 kaug[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
     const int key = key0 + 32 * kt;
+    float part = 0.f;
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
+    for (int s = 0; s < DS; ++s) {
       kreg[kt][s] = key < N ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * s + 8 * hl)
                             : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)kreg[kt][s][e];
+        part = fmaf(x, x, part);
+      }
+    }
+    const float nk = part + xor32(part);
+    const __bf16 n0 = (__bf16)nk;
+    const float r1 = nk - (float)n0;
+    const __bf16 n1 = (__bf16)r1;
+    const __bf16 n2 = (__bf16)(r1 - (float)n1);
+    const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
+    kaug[kt] = hl == 0 ? bf16x8{one, one, one, n0, n1, n2, zero, zero} : bf16x8{};
   }
 
-  float best[KTW];
-  int bidx[KTW];
+  // The centroid chunks are staged after the key loads are issued, so waiting for a chunk
+  // (vmcnt counts in issue order) never waits for more than the loads issued after it.
+  stage(0, mu_s0, aug_s0);
+  if (nchunks > 1) stage(1, mu_s1, aug_s1);
+
+  int bestp[KTW], bbase[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
-    best[kt] = kPosInf;
-    bidx[kt] = 0;
+    bestp[kt] = 0x7fffffff;
+    bbase[kt] = 0;
   }
-  for (int c0 = 0; c0 < C; c0 += CH) {
+  // distance tile ct of a staged chunk: D/16 + 1 MFMAs per key tile
+  auto tile_mfma = [&](const char* ms, const char* as, int ct, f32x16 (&acc)[KTW]) {
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) acc[kt] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 a = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kreg[kt][s], acc[kt]);
+    }
+    const bf16x8 a = lds_read_b128(as, (32 * ct + l32) * 16);
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kaug[kt], acc[kt]);
+  };
+  // running packed minimum over the tile starting at centroid cbase; centroids at or past
+  // `limit` (a ragged last tile) are excluded
+  auto tile_min = [&](const f32x16 (&acc)[KTW], int cbase, bool ragged, int limit) {
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      int pk[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // accumulator r holds centroid cbase + 8(r/4) + 4hl + r%4; pack 8(r/4) + r%4
+        pk[r] = (int)((__float_as_uint(acc[kt][r]) & ~0x1fu) | (uint32_t)(8 * (r >> 2) + (r & 3)));
+        if (ragged && cbase + 8 * (r >> 2) + 4 * hl + (r & 3) >= limit) pk[r] = 0x7fffffff;
+      }
+      int m = pk[0];
+#pragma unroll
+      for (int r = 1; r + 1 < 16; r += 2) m = min(m, min(pk[r], pk[r + 1]));
+      m = min(m, pk[15]);
+      if (m < bestp[kt]) {
+        bestp[kt] = m;
+        bbase[kt] = cbase;
+      }
+    }
+  };
+  constexpr int NT = CH / 32;
+  auto compute = [&](int ci, const char* ms, const char* as) {
+    const int c0 = ci * CH;
     const int valid = min(CH, C - c0);
-    __syncthreads();
+    if (valid == CH) {
+      // full chunk, software-pipelined: the MFMAs of tile t+1 run beside the argmin of t
+      f32x16 acc[2][KTW];
+      tile_mfma(ms, as, 0, acc[0]);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = i * 256 + tid;
-      const int row = idx / NCH;
-      const int ch = idx - row * NCH;
-      bf16x8 v = bf16x8{};
-      if (row < valid) v = *reinterpret_cast<const bf16x8*>(Mh + (size_t)(c0 + row) * D + ch * 8);
-      *reinterpret_cast<bf16x8*>(mu_lds + swz_byte<D>(row, ch)) = v;
-    }
-    __syncthreads();
-    {
-      float nrm = 0.f;
+      for (int t = 0; t < NT; ++t) {
+        if (t + 1 < NT) tile_mfma(ms, as, t + 1, acc[(t + 1) & 1]);
+        tile_min(acc[t & 1], c0 + 32 * t, false, 0);
+        if (t + 1 < NT) {
+          __builtin_amdgcn_sched_group_barrier(0x100, ASG_PRE, 0);
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const bf16x8 v = lds_read_b128(mu_lds, swz_byte<D>(tid, ch));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (float)v[e];
-          nrm = fmaf(x, x, nrm);
-        }
-      }
-      norm_lds[tid] = tid < valid ? nrm : kPosInf;
-    }
-    __syncthreads();
-    const int ntile = (valid + 31) / 32;
-    for (int ct = 0; ct < ntile; ++ct) {
-      f32x16 acc[KTW];
-#pragma unroll
-      for (int kt = 0; kt < KTW; ++kt) acc[kt] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 a = lds_read_b128(mu_lds, swz_byte<D>(32 * ct + l32, 2 * s + hl));
-#pragma unroll
-        for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kreg[kt][s], acc[kt]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 nv = *reinterpret_cast<const f32x4*>(norm_lds + 32 * ct + 8 * i + 4 * hl);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = c0 + 32 * ct + 8 * i + 4 * hl + j;
-#pragma unroll
-          for (int kt = 0; kt < KTW; ++kt) {
-            const float dist = fmaf(-2.f, acc[kt][4 * i + j], nv[j]);
-            if (dist < best[kt]) {   // ascending c per lane: ties keep the lower index
-              best[kt] = dist;
-              bidx[kt] = c;
-            }
+          for (int g = 0; g < DS + 1; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, KTW, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
           }
         }
       }
+    } else {
+      const int ntile = (valid + 31) / 32;
+      for (int ct = 0; ct < ntile; ++ct) {
+        f32x16 acc[KTW];
+        tile_mfma(ms, as, ct, acc);
+        tile_min(acc, c0 + 32 * ct, 32 * ct + 32 > valid, c0 + valid);
+      }
+    }
+  };
+  // Chunk ci sits in buffer ci % 2. Before computing it, each thread waits only until its
+  // loads of chunk ci are done (the next chunk's may still be in flight), then the
+  // workgroup meets; once every wave is done with a buffer, chunk ci + 2 streams into it.
+  auto wait_chunk = [&](bool next_in_flight) {
+    if (next_in_flight) {
+      if (w * 64 < CH) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_T + 1));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_T));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    wait_chunk(ci + 1 < nchunks);
+    compute(ci, mu_s0, aug_s0);
+    if (ci + 1 < nchunks) {
+      __builtin_amdgcn_s_barrier();   // every wave is done with buffer 0
+      if (ci + 2 < nchunks) stage(ci + 2, mu_s0, aug_s0);
+      wait_chunk(ci + 2 < nchunks);
+      compute(ci + 1, mu_s1, aug_s1);
+      if (ci + 3 < nchunks) {
+        __builtin_amdgcn_s_barrier();   // every wave is done with buffer 1
+        stage(ci + 3, mu_s1, aug_s1);
+      }
     }
   }
+
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
-    const float ob = xor32(best[kt]);
-    const int oi = __shfl_xor(bidx[kt], 32, 64);
-    int bi = bidx[kt];
-    if (ob < best[kt] || (ob == best[kt] && oi < bi)) bi = oi;
+    const int mv = bestp[kt] & ~0x1f;
+    const int mc = bbase[kt] + (bestp[kt] & 0x1f) + 4 * hl;
+    const int ov = __shfl_xor(mv, 32, 64);
+    const int oc = __shfl_xor(mc, 32, 64);
+    const int bi = (ov < mv || (ov == mv && oc < mc)) ? oc : mc;
     const int key = key0 + 32 * kt;
     if (hl == 0 && key < N) assign[(size_t)h * N + key] = bi;
   }
@@ -394,9 +543,16 @@ counts_kernel(const uint8_t* __restrict__ hist, const int32_t* __restrict__ size
 template <int D>
 static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL((assign_bf16_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.mu_in),
-                       a.assign, a.N, a.C);
+  {
+    uint16_t* mup = a.cop;
+    uint16_t* aug = a.cop + (size_t)a.H * a.C * D;
+    hipLaunchKernelGGL((centroid_operands_kernel<D>), dim3((a.C + 255) / 256, a.H), dim3(256), 0,
+                       s, static_cast<const uint16_t*>(a.mu_in), mup, aug, a.C);
+    constexpr int AW = ASG_WAVES;
+    hipLaunchKernelGGL((assign_bf16_kernel<D, AW, ASG_CH>), dim3((a.N + AW * 64 - 1) / (AW * 64), a.H),
+                       dim3(AW * 64), 0, s, static_cast<const uint16_t*>(a.K), mup, aug, a.assign,
+                       a.N, a.C);
+  }
   else
     hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,
                        static_cast<const float*>(a.K), static_cast<const float*>(a.mu_in),
