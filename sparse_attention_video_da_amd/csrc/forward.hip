@@ -1,12 +1,13 @@
 // Fused decoupled sparse attention forward for gfx950.
 //
-// One workgroup owns one (head, query block). It walks the query block's exact key blocks
-// (the plan's sorted list) and then the cluster-cache tiles (C centroid keys / mean values
-// taken BLK at a time), treating both the same way: the tile's keys and values are staged
-// in LDS, scores come from MFMA, and a single online softmax (exp2 domain) absorbs every
-// tile. Cluster tiles add a per-key logit bias log2(n[b][c]) (-inf where n = 0), which in
-// the natural-log domain is the ln-count weight of the DecoupAttn abstract: each cluster
-// stands in for the n of its keys left outside the exact blocks.
+// A workgroup walks exact key blocks (the plan's sorted lists) and then the cluster-cache
+// tiles (C centroid keys / mean values taken BLK at a time), treating both the same way:
+// the tile's keys and values are staged in LDS, scores come from MFMA, and a single online
+// softmax (exp2 domain) absorbs every tile. Cluster tiles add a per-key logit bias
+// log2(n[b][c]) (-inf where n = 0), which in the natural-log domain is the ln-count weight
+// of the DecoupAttn abstract: each cluster stands in for the n of its keys left outside the
+// exact blocks. The bf16 kernel gives a workgroup two adjacent query blocks (their exact
+// lists merged); the fp32 kernel one query block.
 //
 // Work split (bf16): wave w handles 32 query rows. Scores are formed transposed,
 // S^T = K * Q^T, so every lane owns one query column and the row max / row sum need only

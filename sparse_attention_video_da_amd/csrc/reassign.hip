@@ -3,8 +3,10 @@
 // counts n[b][c] (keys of cluster c outside query block b's exact key blocks).
 //
 // Kernel sequence per call (one stream, no host synchronisation):
+//   0. operands      (bf16) per centroid: -2 mu and the split |mu|^2 row for the MFMA.
 //   1. assign        MFMA distance product against LDS-staged centroid chunks, per-lane
-//                    running argmin (ties to the lowest index), written as int32.
+//                    running argmin, written as int32 (bf16: any centroid within the
+//                    1e-4 relative tie band of the nearest; fp32: lowest index on ties).
 //   2. block_hist    per key block, an LDS-atomic histogram of its keys' clusters.
 //   3. col_scan      per cluster, exclusive prefix of the histograms over key blocks
 //                    (where each block's keys start inside the cluster) and the sizes.
