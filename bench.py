@@ -197,8 +197,10 @@ def main():
     log(f"[bench] {args.steps} steps: wall {wall_ms:.3f} ms/step, reassign {re_ms:.3f} ms, "
         f"forward {fw_ms:.3f} ms (median {fw_med:.3f})")
 
-    pairs = int(mask.sum()) if mask.shape[0] == 1 else int(mask.sum()) // H
-    exact_flop = 4.0 * B * B * d * pairs * H
+    # exact (query block, key block) pairs over all heads: one shared mask or one per head
+    pairs_all = int(mask.sum()) * (H if mask.shape[0] == 1 else 1)
+    pairs = pairs_all / H
+    exact_flop = 4.0 * B * B * d * pairs_all
     comp_flop = 4.0 * N * C * d * H
     dense_flop = 4.0 * N * N * d * H
     peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -225,7 +227,8 @@ def main():
         "config": {"workload": cfg.name, "heads": H, "seq_len": N, "latent": [cfg.frames,
                    cfg.height, cfg.width], "head_dim": d, "block": B, "clusters": C,
                    "exact_blocks_per_row": cfg.blocks_per_row,
-                   "density": round(pairs / (nb * nb), 4), "parallelism": "single GPU"},
+                   "density": round(pairs / (nb * nb), 4), "mask_heads": int(mask.shape[0]),
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel": "fwd_bf16_kernel<128,128>" if

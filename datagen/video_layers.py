@@ -13,11 +13,16 @@ Every random stream is seeded with numpy's SeedSequence over the tuple
 Streams: 0 centres, 1 K components, 2 K noise, 3 Q components, 4 Q noise, 5 V,
 6 K drift, 7 V drift, 8 mask, 9 cache seed.
 
-The mask is a plan input: position-fixed exact key blocks per query block. Two kinds:
+The mask is a plan input: position-fixed exact key blocks per query block. Three kinds:
   * "random": the diagonal block plus (k - 1) distinct seeded other blocks per row;
   * "local": the k key blocks nearest in a 3D sense, distance^2 between block centres
     (S*df)^2 + dr^2 + dw^2 with S = Hs / 4, ties to the smaller block index; optionally
-    every block holding a token of frame 0 is kept first ("first-frame" blocks).
+    every block holding a token of frame 0 is kept first ("first-frame" blocks);
+  * "local_budget": the same nearest-block rule with a budget k[h][b] per head and query
+    block (one mask per head). Budgets are k times a head factor and a block factor, each
+    log-uniform in [1/2, 2] and seeded per head, rescaled so their mean over the layer is
+    k, rounded and clipped to [1, nb]: the shape of a per-head, per-block budget allocation
+    such as the pages' Distortion Budget produces, with synthetic numbers.
 
 Nothing here computes attention, distances to centroids, cluster means or counts.
 """
@@ -45,8 +50,8 @@ class LayerConfig:
     head_dim: int
     block: int
     clusters: int
-    mask_kind: str          # "random" | "local"
-    blocks_per_row: int     # k = |E_b|
+    mask_kind: str          # "random" | "local" | "local_budget"
+    blocks_per_row: int     # k = |E_b| (the mean budget for "local_budget")
     first_frame: bool       # force blocks holding frame-0 tokens (local masks only)
     mixture: int            # G
     sigma: float
@@ -97,6 +102,20 @@ CONFIGS: Dict[str, LayerConfig] = {
         mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False, drift_v=False,
         description="24 heads, N=118800 (33x45x80), d=128, block 128, C=512, 5% 3D-local "
                     "mask"),
+    "small_budget_bf16": LayerConfig(
+        "small_budget_bf16", 6, heads=6, frames=8, height=32, width=32, head_dim=128,
+        block=128, clusters=128, mask_kind="local_budget", blocks_per_row=12,
+        first_frame=False, mixture=64, sigma=0.3, dtype="bf16", steps=0, drift_k=False,
+        drift_v=False,
+        description="6 heads, N=8192 (8x32x32), d=128, block 128, C=128, per-head and "
+                    "per-block budgets around 12 of 64 key blocks (3D-local)"),
+    "hunyuan13b_budget_bf16": LayerConfig(
+        "hunyuan13b_budget_bf16", 7, heads=24, frames=33, height=45, width=80, head_dim=128,
+        block=128, clusters=512, mask_kind="local_budget", blocks_per_row=46,
+        first_frame=False, mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False,
+        drift_v=False,
+        description="13B-class layer with per-head and per-block budgets averaging 46 of "
+                    "929 key blocks (5% density), one 3D-local mask per head"),
     "extreme_cache_bf16": LayerConfig(
         "extreme_cache_bf16", 5, heads=40, frames=21, height=45, width=80, head_dim=128,
         block=128, clusters=512, mask_kind="local", blocks_per_row=6, first_frame=False,
@@ -185,11 +204,46 @@ def _block_centres(cfg: LayerConfig) -> np.ndarray:
     return cen
 
 
+def budgets(cfg: LayerConfig) -> np.ndarray:
+    """int [H][nb] exact-block budgets of a "local_budget" layer (see the module notes)."""
+    nb, k = cfg.num_blocks, cfg.blocks_per_row
+    f = np.empty((cfg.heads, nb))
+    for h in range(cfg.heads):
+        rng = _rng(cfg, h, STREAM_MASK)
+        head = np.exp(rng.uniform(-math.log(2.0), math.log(2.0)))
+        f[h] = head * np.exp(rng.uniform(-math.log(2.0), math.log(2.0), size=nb))
+    f *= k / f.mean()
+    return np.clip(np.rint(f), 1, nb).astype(np.int64)
+
+
+def _local_orders(cfg: LayerConfig) -> np.ndarray:
+    """[nb][nb] key blocks of each query block by 3D distance, ties to the smaller index."""
+    nb = cfg.num_blocks
+    cen = _block_centres(cfg)
+    s = cfg.local_scale
+    idx = np.arange(nb)
+    out = np.empty((nb, nb), dtype=np.int64)
+    for b in range(nb):
+        diff = cen - cen[b]
+        dist2 = (s * diff[:, 0]) ** 2 + diff[:, 1] ** 2 + diff[:, 2] ** 2
+        out[b] = np.lexsort((idx, dist2))
+    return out
+
+
 def block_mask(cfg: LayerConfig) -> np.ndarray:
-    """uint8 [1][nb][nb]; nonzero = key block computed exactly for that query block."""
+    """uint8 [1][nb][nb] (or [H][nb][nb] for per-head budgets); nonzero = key block computed
+    exactly for that query block."""
     nb, k = cfg.num_blocks, cfg.blocks_per_row
     if not 1 <= k <= nb:
         raise ValueError("blocks_per_row out of range")
+    if cfg.mask_kind == "local_budget":
+        kk = budgets(cfg)
+        order = _local_orders(cfg)
+        mask = np.zeros((cfg.heads, nb, nb), dtype=np.uint8)
+        for h in range(cfg.heads):
+            for b in range(nb):
+                mask[h, b, order[b, : kk[h, b]]] = 1
+        return mask
     mask = np.zeros((nb, nb), dtype=np.uint8)
     if cfg.mask_kind == "random":
         rng = _rng(cfg, 0, STREAM_MASK)

@@ -28,6 +28,10 @@ struct da_plan_s {
   std::vector<int32_t> prowptr;  // [mask_heads][npairs + 1]
   std::vector<int32_t> pcol;
   int32_t npairs = 0;
+  // bf16 forward schedule: work items (head, pair) in natural order split into 8
+  // contiguous ranges of about equal work, range x for XCD x
+  int32_t xstart[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t xmax = 0;
   int32_t* d_rowptr = nullptr;
   int32_t* d_col = nullptr;
   int32_t* d_prowptr = nullptr;
@@ -147,6 +151,31 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
       }
     }
     p->prowptr[(size_t)mh * (npairs + 1) + npairs] = (int32_t)p->pcol.size();
+  }
+  // Balanced split of the forward's work items over the 8 XCDs (workgroup ids are dealt to
+  // XCDs round-robin). An item's work is its tile count: the union of the pair's exact
+  // lists plus the cluster tiles, plus one tile for its prologue and epilogue. Contiguous
+  // ranges keep neighbouring query blocks, which share key blocks, on one L2; equal work
+  // per range keeps the XCDs busy equally long when budgets differ across heads or blocks.
+  {
+    const int64_t items = (int64_t)desc->heads * npairs;
+    const int32_t ctiles = (desc->clusters + desc->block - 1) / desc->block;
+    std::vector<int64_t> pre((size_t)items + 1, 0);
+    for (int64_t i = 0; i < items; ++i) {
+      const int32_t h = (int32_t)(i / npairs), pr = (int32_t)(i % npairs);
+      const size_t base = (size_t)(desc->mask_heads == 1 ? 0 : h) * (npairs + 1);
+      const int64_t len = p->prowptr[base + pr + 1] - p->prowptr[base + pr];
+      pre[(size_t)i + 1] = pre[(size_t)i] + len + ctiles + 1;
+    }
+    int64_t at = 0;
+    p->xstart[0] = 0;
+    for (int x = 1; x < 8; ++x) {
+      const int64_t target = (pre[(size_t)items] * x + 4) / 8;
+      while (at < items && pre[(size_t)at + 1] <= target) ++at;
+      p->xstart[x] = (int32_t)at;
+    }
+    p->xstart[8] = (int32_t)items;
+    for (int x = 0; x < 8; ++x) p->xmax = std::max(p->xmax, p->xstart[x + 1] - p->xstart[x]);
   }
 
   int ndev = 0;
@@ -297,6 +326,8 @@ DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void*
   a.prowptr = p->d_prowptr;
   a.pcol = p->d_pcol;
   a.npairs = p->npairs;
+  for (int x = 0; x < 9; ++x) a.xstart[x] = p->xstart[x];
+  a.xmax = p->xmax;
   a.O = O;
   a.lse = lse_out;
   a.H = d.heads;

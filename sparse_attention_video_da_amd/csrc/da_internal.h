@@ -19,6 +19,8 @@ struct FwdArgs {
   const int32_t* prowptr; // [mask_heads][npairs + 1] lists of query-block pairs (2p, 2p+1)
   const int32_t* pcol;    // union of the pair's exact blocks: kb | (in 2p) << 28 | (in 2p+1) << 29
   int npairs;
+  int xstart[9];         // items (h * npairs + pair) xstart[x] .. xstart[x+1]-1 run on XCD x
+  int xmax;              // largest range
   void* O;
   float* lse;            // may be null
   int H, N, C, nb, mask_heads;

@@ -125,11 +125,12 @@ fwd_bf16_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) float bias_s0[2 * BLK];   // [half][BLK]
   __shared__ __attribute__((aligned(16))) float bias_s1[2 * BLK];
 
-  const int total = p.H * p.npairs;
-  const int logical = xcd_remap(blockIdx.x, total);
-  if (logical >= total) return;
-  const int h = logical / p.npairs;
-  const int pr = logical - h * p.npairs;
+  // workgroup id L runs on XCD L % 8 and takes the next item of that XCD's range
+  const int xcd = blockIdx.x & 7;
+  const int item = p.xstart[xcd] + (int)(blockIdx.x >> 3);
+  if (item >= p.xstart[xcd + 1]) return;
+  const int h = item / p.npairs;
+  const int pr = item - h * p.npairs;
   const int b0 = 2 * pr;
 
   const int tid = threadIdx.x;
@@ -588,8 +589,7 @@ template <int D, int BLK>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool bf16, hipStream_t stream) {
   const size_t lds = fwd_lds_bytes<D, BLK>(bf16);
   if (bf16) {
-    const int total = a.H * a.npairs;
-    const int grid = ((total + 7) / 8) * 8;
+    const int grid = 8 * a.xmax;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 4), 0, stream, a);
   } else {
     const int total = a.H * a.nb;

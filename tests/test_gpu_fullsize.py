@@ -47,7 +47,7 @@ def _step(lib, plan, cfg, L, mu0_stored, heads, qblocks, what):
     torch = torch_mod()
     dt = cfg.dtype
     B, C = cfg.block, cfg.clusters
-    mask = L["mask"][0]
+    mask_h = (lambda h: L["mask"][0] if L["mask"].shape[0] == 1 else L["mask"][h])
     say(f"[case] {what}: H={cfg.heads} N={cfg.seq_len} C={C} heads={heads}")
     dev = {x: to_dev(L[x], dt) for x in ("Q", "K", "V")}
     out = plan.reassign(dev["K"], dev["V"], to_dev(mu0_stored, dt))
@@ -62,7 +62,7 @@ def _step(lib, plan, cfg, L, mu0_stored, heads, qblocks, what):
                "counts": out["counts"][h].cpu().numpy(),
                "centroids": from_dev(out["centroids"][h], dt),
                "mean_values": from_dev(out["mean_values"][h], dt)}
-        r = check_reassign_head(K64, V64, mu0, mask, B, dt, got, f"{what} head {h}")
+        r = check_reassign_head(K64, V64, mu0, mask_h(h), B, dt, got, f"{what} head {h}")
         moves += r["band_moves"]
         caches[h] = r["ref"]
     say(f"  reassign ok on {len(heads)} heads ({moves} in-band moves)")
@@ -81,14 +81,14 @@ def _step(lib, plan, cfg, L, mu0_stored, heads, qblocks, what):
     for h in heads:
         ref, _ = O.forward(O.to_f64(L["Q"][h], dt), O.to_f64(L["K"][h], dt),
                            O.to_f64(L["V"][h], dt), caches[h]["mu1"], caches[h]["vbar"],
-                           caches[h]["counts"], mask, B, qblocks=qblocks)
+                           caches[h]["counts"], mask_h(h), B, qblocks=qblocks)
         got_all.append(from_dev(o[h][torch.from_numpy(rows).cuda()], dt))
         want_all.append(ref[rows])
     check_forward(np.concatenate(got_all), np.concatenate(want_all), dt, f"{what} forward")
     return caches, out["centroids"]
 
 
-@pytest.mark.parametrize("name", ["wan14b_bf16", "hunyuan13b_bf16"])
+@pytest.mark.parametrize("name", ["wan14b_bf16", "hunyuan13b_bf16", "hunyuan13b_budget_bf16"])
 def test_full_layer(lib, name):
     cfg = get_config(name)
     L = make_layer(cfg, threads=16)

@@ -98,8 +98,9 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
         lg.append(lse[h])
         lw.append(ref_lse)
     check_forward(np.concatenate(got_all), np.concatenate(want_all), dtype, f"{what} forward")
-    # lse tolerance: bf16 probabilities are rounded (RNE) to 8 significant bits before they
-    # are summed into the denominator, so ln l can move by at most ln(1 + 2^-8) < 4e-3
+    # lse tolerance (bf16): ln(1 + 2^-8) < 4e-3 bounds the change if every probability in
+    # the row sum carried a full bf16 rounding error (8 significant bits, RNE); the kernel
+    # sums fp32 probabilities and stays well inside it
     lse_err = float(np.max(np.abs(np.concatenate(lg) - np.concatenate(lw))))
     say(f"  {what} lse: max_abs={lse_err:.3e}")
     assert lse_err <= (4e-3 if dtype == "bf16" else 1e-5), lse_err
@@ -132,6 +133,17 @@ def test_small_bf16_config(lib):
                                            O.to_f64(L["cache_init"][h], "bf16"), 10, "bf16"),
                             "bf16") for h in range(cfg.heads)])
     _run_case(lib, L, mu0, L["mask"], _cfgd(cfg), "small_bf16")
+
+
+def test_small_budget_config(lib):
+    """6 heads, N=8192, d=128, bf16, C=128, one mask per head with per-head and per-block
+    exact budgets (3..39 of 64 key blocks): every head and query block checked, so a
+    scheduling slip that skips or repeats work items shows up."""
+    cfg = get_config("small_budget_bf16")
+    L = make_layer(cfg)
+    assert L["mask"].shape[0] == cfg.heads
+    assert len(set(L["mask"].sum(axis=(1, 2)).tolist())) > 1   # budgets differ across heads
+    _run_case(lib, L, L["cache_init"], L["mask"], _cfgd(cfg), "small_budget_bf16")
 
 
 # ----------------------------------------------------------------- ragged / edge shapes
