@@ -193,7 +193,9 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     re_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     fw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    fw_med = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    fw_all = [e[1].elapsed_time(e[2]) for e in evs]
+    re_all = [e[0].elapsed_time(e[1]) for e in evs]
+    fw_med = float(np.median(fw_all))
     log(f"[bench] {args.steps} steps: wall {wall_ms:.3f} ms/step, reassign {re_ms:.3f} ms, "
         f"forward {fw_ms:.3f} ms (median {fw_med:.3f})")
 
@@ -238,7 +240,12 @@ def main():
                                     "key block) pair"},
         "breakdown": {
             "forward_ms": round(fw_ms, 4), "forward_ms_median": round(fw_med, 4),
+            "forward_ms_p10_p90": [round(float(np.percentile(fw_all, 10)), 4),
+                                   round(float(np.percentile(fw_all, 90)), 4)],
             "reassign_ms": round(re_ms, 4),
+            "reassign_ms_median": round(float(np.median(re_all)), 4),
+            "reassign_ms_p10_p90": [round(float(np.percentile(re_all, 10)), 4),
+                                    round(float(np.percentile(re_all, 90)), 4)],
             "forward_tflops_exact": round(achieved, 1),
             "forward_tflops_exact_plus_compensation": round(
                 (exact_flop + comp_flop) / (fw_ms * 1e-3) / 1e12, 1),
