@@ -41,6 +41,7 @@ struct da_plan_s {
   int32_t* d_start = nullptr;
   int32_t* d_perm = nullptr;
   int32_t* d_cop = nullptr;
+  int32_t* d_part = nullptr;
   int64_t bytes = 0;
   int device = 0;
 };
@@ -79,11 +80,12 @@ da_status check_desc(const da_desc* d) {
 
 void destroy_device(da_plan_s* p) {
   int32_t* bufs[] = {p->d_rowptr, p->d_col,   p->d_prowptr, p->d_pcol,
-                     p->d_hist,   p->d_off,   p->d_start,   p->d_perm, p->d_cop};
+                     p->d_hist,   p->d_off,   p->d_start,   p->d_perm, p->d_cop,
+                     p->d_part};
   for (int32_t* b : bufs)
     if (b) (void)hipFree(b);
   p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
-  p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = nullptr;
+  p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = p->d_part = nullptr;
 }
 
 std::once_flag g_prep_once;
@@ -199,7 +201,8 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
       {&p->d_rowptr, n_rowptr},   {&p->d_col, n_col},   {&p->d_prowptr, n_prowptr},
       {&p->d_pcol, n_pcol},       {&p->d_hist, (H * nb * C + 3) / 4}, {&p->d_off, H * nb * C},
       {&p->d_start, H * C},       {&p->d_perm, H * N},
-      {&p->d_cop, (H * C * ((size_t)desc->head_dim + 8) * 2 + 3) / 4}};
+      {&p->d_cop, (H * C * ((size_t)desc->head_dim + 8) * 2 + 3) / 4},
+      {&p->d_part, H * ((N + 255) / 256 + C) * 2 * (size_t)desc->head_dim}};
   for (const Alloc& a : allocs) {
     if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -286,11 +289,15 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
   a.counts = qblock_counts_out;
   a.rowptr = p->d_rowptr;
   a.col = p->d_col;
+  a.prowptr = p->d_prowptr;
+  a.pcol = p->d_pcol;
+  a.npairs = p->npairs;
   a.hist = reinterpret_cast<uint8_t*>(p->d_hist);
   a.off = p->d_off;
   a.start = p->d_start;
   a.perm = p->d_perm;
   a.cop = reinterpret_cast<uint16_t*>(p->d_cop);
+  a.part = reinterpret_cast<float*>(p->d_part);
   a.H = d.heads;
   a.N = d.seq_len;
   a.C = d.clusters;

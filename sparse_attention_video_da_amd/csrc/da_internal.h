@@ -38,11 +38,15 @@ struct ReassignArgs {
   int32_t* counts;
   const int32_t* rowptr;
   const int32_t* col;
+  const int32_t* prowptr;  // query-block pair lists (as in FwdArgs)
+  const int32_t* pcol;
+  int npairs;
   uint8_t* hist;   // workspace [H][nb][C] per-block cluster histograms (<= block keys)
   int32_t* off;    // workspace [H][nb][C]
   int32_t* start;  // workspace [H][C]
   int32_t* perm;   // workspace [H][N]
   uint16_t* cop;   // workspace: bf16 distance operands, [H][C][D] (-2 mu) then [H][C][8]
+  float* part;     // workspace [H][ceil(N / 256) + C][2][D] partial sums of K and V
   int H, N, C, nb, block, mask_heads;
 };
 

@@ -13,9 +13,10 @@
 //   4. starts        per head, exclusive prefix of the sizes over clusters.
 //   5. scatter       key index -> slot start[c] + off[kb][c] + rank within the block, so
 //                    every cluster's keys sit contiguously in ascending key order.
-//   6. cluster_sum   one wave per cluster sums its keys and values in that fixed order
-//                    (fp32, deterministic), divides, rounds to the cache dtype.
-//   7. counts        n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c].
+//   6. sums          fixed-size segments of the sorted order give fp32 partial sums per
+//                    cluster run, then one wave per cluster adds its partials in order,
+//                    divides and rounds to the cache dtype (deterministic throughout).
+//   7. counts        n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c], per pair.
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -79,8 +80,9 @@ centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | ((n >> 4) << 14); }
 
-// 8 waves x 64 keys per workgroup (2 key tiles of 32 per wave). Centroid chunks of CH are
-// staged in swizzled LDS by direct buffer loads, two chunks at a time. The score tile
+// WAVES waves x 64 keys per workgroup (2 key tiles of 32 per wave; 4 waves, two
+// workgroups per CU, by default). Centroid chunks of CH (128 by default) stream into two
+// swizzled LDS buffers by direct buffer loads, each waited for on its own. The score tile
 // D^T = mu * K^T gives each lane one key and 16 centroids per 32-centroid tile; the lane
 // packs a 5-bit tile-local index into the low mantissa bits of each distance (a change
 // below 2^-18 relative, far inside the 1e-4 tie band) and keeps the integer minimum with
@@ -418,27 +420,54 @@ scatter_kernel(const int32_t* __restrict__ assign, const int32_t* __restrict__ o
 }
 
 // ----------------------------------------------------------------------------- 6. sums
-// One wave per cluster; each lane owns D/64 consecutive dims. Keys are visited in the
-// scattered (ascending) order, 8 rows in flight.
+// Two phases with balanced work whatever the cluster sizes. Phase 1: wave s sums the keys
+// and values at sorted positions [s*SEG, (s+1)*SEG) (clusters are contiguous there, in
+// ascending key order), writing one fp32 partial per cluster run it meets into slot s + c:
+// unique, because a cluster that reaches segment s+1 ends before cluster c+1 starts. Phase 2:
+// one wave per cluster adds its partials in segment order, divides and rounds. Every sum
+// runs in a fixed order, so results are bit-reproducible. Each lane owns D/64 dims.
+constexpr int kSeg = 256;
+#ifndef SEG_U
+#define SEG_U 16
+#endif
+
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256)
-cluster_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
-                   const void* __restrict__ mu_in, void* __restrict__ mu_out,
-                   void* __restrict__ vbar_out, const int32_t* __restrict__ sizes,
-                   const int32_t* __restrict__ start, const int32_t* __restrict__ perm, int N,
-                   int C) {
+segment_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
+                   const int32_t* __restrict__ sizes, const int32_t* __restrict__ start,
+                   const int32_t* __restrict__ perm, float* __restrict__ part, int N, int C,
+                   int nseg) {
   constexpr int EPL = D / 64;
-  constexpr int U = 16;
+  constexpr int U = SEG_U;
   const int h = blockIdx.y;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + w;
-  if (c >= C) return;
-  const int cnt = sizes[(size_t)h * C + c];
-  const int32_t* pl = perm + (size_t)h * N + start[(size_t)h * C + c];
+  const int lane = threadIdx.x & 63;
+  const int sgi = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sgi >= nseg) return;
+  const int p0 = sgi * kSeg, p1 = min(N, p0 + kSeg);
+  const int32_t* st = start + (size_t)h * C;
+  const int32_t* sz = sizes + (size_t)h * C;
+  const int32_t* pl = perm + (size_t)h * N;
+  // cluster holding position p0: the last c with start[c] <= p0 (it is non-empty)
+  int lo = 0, hi = C - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (st[mid] <= p0) lo = mid; else hi = mid - 1;
+  }
+  int c = lo;
+  int cend = st[c] + sz[c];
   float ks[EPL], vs[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ks[e] = vs[e] = 0.f;
-
+  float* ph = part + (size_t)h * (nseg + C) * 2 * D;
+  auto flush = [&]() {
+    float* o = ph + (size_t)(sgi + c) * 2 * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      o[e] = ks[e];
+      o[D + e] = vs[e];
+      ks[e] = vs[e] = 0.f;
+    }
+  };
   auto load_row = [&](const void* base, int j, float* out) {
     if constexpr (BF16) {
       const uint16_t* r = static_cast<const uint16_t*>(base) + ((size_t)h * N + j) * D + lane * EPL;
@@ -455,33 +484,61 @@ cluster_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
       for (int e = 0; e < EPL; ++e) out[e] = r[e];
     }
   };
-
-  int i = 0;
-  for (; i + U <= cnt; i += U) {
+  for (int i = p0; i < p1; i += U) {
+    const int n = min(U, p1 - i);
     float kr[U][EPL], vr[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = pl[i + u];
+      const int j = pl[i + min(u, n - 1)];
       load_row(Kv, j, kr[u]);
       load_row(Vv, j, vr[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (u < n) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          ks[e] += kr[u][e];
+          vs[e] += vr[u][e];
+        }
+        if (i + u + 1 == cend) {   // this cluster's run ends here
+          flush();
+          while (c + 1 < C && st[c + 1] + sz[c + 1] <= i + u + 1) ++c;   // skip empty ones
+          ++c;
+          cend = c < C ? st[c] + sz[c] : N;
+        }
+      }
+    }
+  }
+  if (c < C && st[c] < p1 && p1 < cend) flush();   // a run continuing into the next segment
+}
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256)
+cluster_finish_kernel(const float* __restrict__ part, const void* __restrict__ mu_in,
+                      void* __restrict__ mu_out, void* __restrict__ vbar_out,
+                      const int32_t* __restrict__ sizes, const int32_t* __restrict__ start,
+                      int C, int nseg) {
+  constexpr int EPL = D / 64;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= C) return;
+  const int cnt = sizes[(size_t)h * C + c];
+  float ks[EPL], vs[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ks[e] = vs[e] = 0.f;
+  if (cnt > 0) {
+    const int p0 = start[(size_t)h * C + c];
+    const int s0 = p0 / kSeg, s1 = (p0 + cnt - 1) / kSeg;
+    const float* ph = part + (size_t)h * (nseg + C) * 2 * D + lane * EPL;
+    for (int sg = s0; sg <= s1; ++sg) {
+      const float* q = ph + (size_t)(sg + c) * 2 * D;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        ks[e] += kr[u][e];
-        vs[e] += vr[u][e];
+        ks[e] += q[e];
+        vs[e] += q[D + e];
       }
-  }
-  for (; i < cnt; ++i) {
-    float kr[EPL], vr[EPL];
-    const int j = pl[i];
-    load_row(Kv, j, kr);
-    load_row(Vv, j, vr);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      ks[e] += kr[e];
-      vs[e] += vr[e];
     }
   }
   const size_t o = ((size_t)h * C + c) * D + lane * EPL;
@@ -508,35 +565,66 @@ cluster_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
 }
 
 // ----------------------------------------------------------------------------- 7. counts
-// n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c]; 4 clusters per thread from
-// the byte histograms (one head's histograms stay resident in L2 across its query blocks).
+// n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c], for the two query blocks of
+// a pair at once: the pair's union list (entries kb | in 2p << 28 | in 2p+1 << 29) reads each
+// shared key block's byte histogram once. Each thread owns 2 clusters of both blocks.
 __global__ void __launch_bounds__(256)
 counts_kernel(const uint8_t* __restrict__ hist, const int32_t* __restrict__ sizes,
-              const int32_t* __restrict__ rowptr, const int32_t* __restrict__ col,
-              int32_t* __restrict__ counts, int C, int nb, int mask_heads) {
-  const int h = blockIdx.y, b = blockIdx.x;
+              const int32_t* __restrict__ prowptr, const int32_t* __restrict__ pcol,
+              int32_t* __restrict__ counts, int C, int nb, int npairs, int mask_heads) {
+  const int h = blockIdx.y, pr = blockIdx.x;
+  const int b0 = 2 * pr;
+  const bool has1 = b0 + 1 < nb;
   const int mh = mask_heads == 1 ? 0 : h;
-  const int e0 = rowptr[mh * (nb + 1) + b], e1 = rowptr[mh * (nb + 1) + b + 1];
+  const int e0 = prowptr[mh * (npairs + 1) + pr], e1 = prowptr[mh * (npairs + 1) + pr + 1];
   const uint8_t* hh = hist + (size_t)h * nb * C;
-  int32_t* dst = counts + ((size_t)h * nb + b) * C;
+  int32_t* dst0 = counts + ((size_t)h * nb + b0) * C;
+  int32_t* dst1 = dst0 + C;
   const int32_t* sz = sizes + (size_t)h * C;
-  if ((C & 3) == 0) {
-    for (int c = 4 * threadIdx.x; c < C; c += 4 * 256) {
-      int n0 = sz[c], n1 = sz[c + 1], n2 = sz[c + 2], n3 = sz[c + 3];
-      for (int e = e0; e < e1; ++e) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(hh + (size_t)col[e] * C + c);
-        n0 -= v & 0xff;
-        n1 -= (v >> 8) & 0xff;
-        n2 -= (v >> 16) & 0xff;
-        n3 -= v >> 24;
+  if ((C & 1) == 0) {
+    for (int c = 2 * threadIdx.x; c < C; c += 2 * 256) {
+      int a0 = sz[c], a1 = sz[c + 1];
+      int c0 = a0, c1 = a1;
+      // 8 list entries (wave-uniform) and their histogram rows in flight at a time
+      constexpr int U = 8;
+      int e = e0;
+      for (; e + U <= e1; e += U) {
+        int ent[U];
+        uint32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ent[u] = pcol[e + u];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          v[u] = *reinterpret_cast<const uint16_t*>(hh + (size_t)(ent[u] & 0x0fffffff) * C + c);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int lo = v[u] & 0xff, hi = v[u] >> 8;
+          const int f0 = (ent[u] >> 28) & 1, f1 = (ent[u] >> 29) & 1;
+          a0 -= f0 * lo; a1 -= f0 * hi;
+          c0 -= f1 * lo; c1 -= f1 * hi;
+        }
       }
-      *reinterpret_cast<int4*>(dst + c) = make_int4(n0, n1, n2, n3);
+      for (; e < e1; ++e) {
+        const int ent = pcol[e];
+        const uint32_t v = *reinterpret_cast<const uint16_t*>(hh + (size_t)(ent & 0x0fffffff) * C + c);
+        const int lo = v & 0xff, hi = v >> 8;
+        if (ent & (1 << 28)) { a0 -= lo; a1 -= hi; }
+        if (ent & (1 << 29)) { c0 -= lo; c1 -= hi; }
+      }
+      *reinterpret_cast<int2*>(dst0 + c) = make_int2(a0, a1);
+      if (has1) *reinterpret_cast<int2*>(dst1 + c) = make_int2(c0, c1);
     }
   } else {
     for (int c = threadIdx.x; c < C; c += 256) {
-      int n = sz[c];
-      for (int e = e0; e < e1; ++e) n -= hh[(size_t)col[e] * C + c];
-      dst[c] = n;
+      int a0 = sz[c], c0 = sz[c];
+      for (int e = e0; e < e1; ++e) {
+        const int ent = pcol[e];
+        const int v = hh[(size_t)(ent & 0x0fffffff) * C + c];
+        if (ent & (1 << 28)) a0 -= v;
+        if (ent & (1 << 29)) c0 -= v;
+      }
+      dst0[c] = a0;
+      if (has1) dst1[c] = c0;
     }
   }
 }
@@ -566,16 +654,22 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
   hipLaunchKernelGGL(starts_kernel, dim3(a.H), dim3(1024), 0, s, a.sizes, a.start, a.C);
   hipLaunchKernelGGL(scatter_kernel, dim3(a.nb, a.H), dim3(256), 0, s, a.assign, a.off,
                      a.start, a.perm, a.N, a.C, a.nb, a.block);
-  if (bf16)
-    hipLaunchKernelGGL((cluster_sum_kernel<D, true>), dim3((a.C + 3) / 4, a.H), dim3(256), 0, s,
-                       a.K, a.V, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.perm, a.N,
-                       a.C);
-  else
-    hipLaunchKernelGGL((cluster_sum_kernel<D, false>), dim3((a.C + 3) / 4, a.H), dim3(256), 0,
-                       s, a.K, a.V, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.perm,
-                       a.N, a.C);
-  hipLaunchKernelGGL(counts_kernel, dim3(a.nb, a.H), dim3(256), 0, s, a.hist, a.sizes,
-                     a.rowptr, a.col, a.counts, a.C, a.nb, a.mask_heads);
+  {
+    const int nseg = (a.N + kSeg - 1) / kSeg;
+    if (bf16) {
+      hipLaunchKernelGGL((segment_sum_kernel<D, true>), dim3((nseg + 3) / 4, a.H), dim3(256), 0,
+                         s, a.K, a.V, a.sizes, a.start, a.perm, a.part, a.N, a.C, nseg);
+      hipLaunchKernelGGL((cluster_finish_kernel<D, true>), dim3((a.C + 3) / 4, a.H), dim3(256),
+                         0, s, a.part, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.C, nseg);
+    } else {
+      hipLaunchKernelGGL((segment_sum_kernel<D, false>), dim3((nseg + 3) / 4, a.H), dim3(256), 0,
+                         s, a.K, a.V, a.sizes, a.start, a.perm, a.part, a.N, a.C, nseg);
+      hipLaunchKernelGGL((cluster_finish_kernel<D, false>), dim3((a.C + 3) / 4, a.H), dim3(256),
+                         0, s, a.part, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.C, nseg);
+    }
+  }
+  hipLaunchKernelGGL(counts_kernel, dim3(a.npairs, a.H), dim3(256), 0, s, a.hist, a.sizes,
+                     a.prowptr, a.pcol, a.counts, a.C, a.nb, a.npairs, a.mask_heads);
   return hipGetLastError();
 }
 
