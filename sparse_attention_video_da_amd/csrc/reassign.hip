@@ -23,9 +23,6 @@
 namespace da {
 
 constexpr float kPosInf = __builtin_inff();
-#ifndef ASG_PRE
-#define ASG_PRE 4
-#endif
 #ifndef ASG_WAVES
 #define ASG_WAVES 4
 #endif
@@ -221,15 +218,35 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
     const int c0 = ci * CH;
     const int valid = min(CH, C - c0);
     if (valid == CH) {
-      // full chunk, software-pipelined: the MFMAs of tile t+1 run beside the argmin of t
+      // full chunk, software-pipelined: the MFMAs of tile t+1 run beside the argmin of t,
+      // and the centroid operands of tile t+2 are read meanwhile into the register set
+      // tile t has just released
       f32x16 acc[2][KTW];
-      tile_mfma(ms, as, 0, acc[0]);
+      bf16x8 ops[2][DS + 1];
+      auto load_ops = [&](int ct, bf16x8 (&o)[DS + 1]) {
+#pragma unroll
+        for (int s = 0; s < DS; ++s) o[s] = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
+        o[DS] = lds_read_b128(as, (32 * ct + l32) * 16);
+      };
+      auto mfma_ops = [&](const bf16x8 (&o)[DS + 1], f32x16 (&acc_)[KTW]) {
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) acc_[kt] = f32x16{};
+#pragma unroll
+        for (int s = 0; s <= DS; ++s)
+#pragma unroll
+          for (int kt = 0; kt < KTW; ++kt)
+            acc_[kt] = mfma32x32x16(o[s], s < DS ? kreg[kt][s] : kaug[kt], acc_[kt]);
+      };
+      load_ops(0, ops[0]);
+      if (NT > 1) load_ops(1, ops[1]);
+      mfma_ops(ops[0], acc[0]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (t + 1 < NT) tile_mfma(ms, as, t + 1, acc[(t + 1) & 1]);
+        if (t + 1 < NT) mfma_ops(ops[(t + 1) & 1], acc[(t + 1) & 1]);
+        if (t + 2 < NT) load_ops(t + 2, ops[t & 1]);
         tile_min(acc[t & 1], c0 + 32 * t, false, 0);
         if (t + 1 < NT) {
-          __builtin_amdgcn_sched_group_barrier(0x100, ASG_PRE, 0);
 #pragma unroll
           for (int g = 0; g < DS + 1; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, KTW, 0);
@@ -237,6 +254,7 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       const int ntile = (valid + 31) / 32;
