@@ -43,6 +43,15 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m sparse_attention_video_da_amd.build`"
             " (there is no non-HIP fallback)")
+    # PyTorch ships its own HIP runtime under the same soname as the system one this library
+    # links. Loading PyTorch first makes the library bind to that one runtime, so the device
+    # pointers and stream handles PyTorch hands over belong to the runtime that uses them;
+    # loading the library first would bring up a second runtime that PyTorch's cannot share
+    # the device with.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32p, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     u8p = ctypes.POINTER(ctypes.c_uint8)
