@@ -166,6 +166,21 @@ def test_ragged_shapes(lib, d, B, dtype, N):
               f"ragged d{d} B{B} {dtype}")
 
 
+@pytest.mark.parametrize("N,C", [(900, 20), (2000, 300), (4000, 2048)])
+def test_cluster_count_edges(lib, N, C):
+    """bf16 cluster counts away from the tile sizes: fewer centroids than one 32-wide
+    distance tile (C = 20), an odd number of 128-centroid staging chunks with a ragged last
+    one (C = 300: 3 chunks), and many chunks with mostly tiny or empty clusters
+    (C = 2048: 16 chunks, about 2 keys per cluster, many refresh segments)."""
+    H, d, B = 2, 128, 128
+    L, cache = _random_layer(300 + C, H, N, d, "bf16", C, G=max(2, C // 4))
+    nb = -(-N // B)
+    rng = np.random.default_rng(C)
+    mask = (rng.random((1, nb, nb)) < 0.35).astype(np.uint8)
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype="bf16"),
+              f"clusters C={C} N={N}")
+
+
 def test_all_blocks_exact_is_dense(lib):
     """Every block exact: the GPU output is dense attention (oracle's dense routine)."""
     torch = torch_mod()
