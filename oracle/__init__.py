@@ -9,7 +9,9 @@ none of the method's arithmetic.
 Source of every definition: the DecoupAttn abstract ("DecoupAttn: Decoupled Sparse
 Attention for Training-Free Acceleration of Video Diffusion", arXiv 2611.05917, Abstract),
 and Lloyd, "Least squares quantization in PCM" (listed on that paper page under the works
-it builds on). Each function names the sentence of the abstract it follows.
+it builds on). Each function names the sentence of the abstract it follows. Exact key
+blocks smaller than the query blocks (the optional `kblock`) follow the kernel sentence of
+the Accurate Block Attention (AB-Attention) abstract.
 
 Pinning status: every public function is pinned by tests that do not retype it (closed
 forms, a hand-derived worked example, brute force, invariants and library special cases).

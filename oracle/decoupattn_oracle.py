@@ -1,9 +1,16 @@
 """fp64 reference definitions (test infrastructure only; see the package docstring).
 
 Notation (one attention head at a time):
-  N tokens, head dim d, block size B, nb = ceil(N / B) blocks, blk(j) = j // B,
-  C clusters, mask[b][kb] != 0 when key block kb is computed exactly for query block b,
-  E_b = {kb : mask[b][kb] != 0}, scale = 1 / sqrt(d) unless given.
+  N tokens, head dim d, query block size B, nb = ceil(N / B) query blocks,
+  key block size S (`kblock`, default S = B), nkb = ceil(N / S) key blocks, blk(j) = j // S,
+  C clusters, mask[b][kb] != 0 when key block kb is computed exactly for query block b
+  (mask is nb x nkb), E_b = {kb : mask[b][kb] != 0}, scale = 1 / sqrt(d) unless given.
+
+Key blocks smaller than the query block (S = B/2, B/4, ...) are the finer exact granularity
+of the Accurate Block Attention (AB-Attention) abstract, whose kernel packs key/value blocks
+smaller than a tile into full tensor-core tiles. Nothing else changes: every key outside
+E_b's key blocks is compensated by its cluster, so the counts n[b][c] are taken over keys,
+whatever the key block size.
 
 Every array handed in is already the exact value of the stored tensor (bf16 or fp32)
 widened to float64; `to_f64` does that widening for the storage formats used here.
@@ -124,15 +131,16 @@ def assignment_allowed(K: np.ndarray, mu: np.ndarray, a_test: np.ndarray,
 
 
 # ----------------------------------------------------------------------------- refresh
-def qblock_counts_direct(a: np.ndarray, mask: np.ndarray, block: int, clusters: int
-                         ) -> np.ndarray:
-    """n[b][c] = number of keys j with a_j = c whose block is NOT exact for query block b.
+def qblock_counts_direct(a: np.ndarray, mask: np.ndarray, block: int, clusters: int,
+                         kblock: Optional[int] = None) -> np.ndarray:
+    """n[b][c] = number of keys j with a_j = c whose key block is NOT exact for query block b.
 
     These are the keys that cluster c stands in for when query block b is attended (the
-    exact blocks stay fixed while every other key is compensated, per the abstract)."""
+    exact blocks stay fixed while every other key is compensated, per the abstract).
+    Key j lies in key block j // S (S = kblock, default the query block size B)."""
     n_tok = len(a)
     nb = mask.shape[0]
-    blk = np.arange(n_tok) // block
+    blk = np.arange(n_tok) // (block if kblock is None else kblock)
     out = np.zeros((nb, clusters), np.int64)
     for b in range(nb):
         outside = mask[b][blk] == 0
@@ -141,7 +149,8 @@ def qblock_counts_direct(a: np.ndarray, mask: np.ndarray, block: int, clusters: 
 
 
 def refresh(K: np.ndarray, V: np.ndarray, a: np.ndarray, mu0: np.ndarray,
-            mask: np.ndarray, block: int, dtype: str) -> Dict[str, np.ndarray]:
+            mask: np.ndarray, block: int, dtype: str, kblock: Optional[int] = None
+            ) -> Dict[str, np.ndarray]:
     """Refresh of the compensation after reassignment (Reassign Cache sentence).
 
     sizes[c] = #{j : a_j = c}
@@ -170,15 +179,16 @@ def refresh(K: np.ndarray, V: np.ndarray, a: np.ndarray, mu0: np.ndarray,
         "vbar_exact": vbar,
         "mu1": storage_round(mu1, dtype),
         "vbar": storage_round(vbar, dtype),
-        "counts": qblock_counts_direct(a, mask, block, c),
+        "counts": qblock_counts_direct(a, mask, block, c, kblock),
     }
 
 
 def reassign_step(K: np.ndarray, V: np.ndarray, mu0: np.ndarray, mask: np.ndarray,
-                  block: int, dtype: str) -> Dict[str, np.ndarray]:
+                  block: int, dtype: str, kblock: Optional[int] = None
+                  ) -> Dict[str, np.ndarray]:
     """One Reassign Cache step: assign every key to the cached centroids, then refresh."""
     a, gap, d1, d2 = assign(K, mu0)
-    out = refresh(K, V, a, mu0, mask, block, dtype)
+    out = refresh(K, V, a, mu0, mask, block, dtype, kblock)
     out.update(assign=a, gap=gap, d1=d1, d2=d2)
     return out
 
@@ -194,12 +204,13 @@ def _exact_keys(mask_row: np.ndarray, block: int, n_tok: int) -> np.ndarray:
 
 def forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mu: np.ndarray, vbar: np.ndarray,
             counts: np.ndarray, mask: np.ndarray, block: int, scale: Optional[float] = None,
-            qblocks: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+            qblocks: Optional[Sequence[int]] = None, kblock: Optional[int] = None
+            ) -> Tuple[np.ndarray, np.ndarray]:
     """Decoupled sparse attention output of one head (abstract: exact attention on a few
     position-fixed blocks, semantic clusters compensating every other key, one softmax).
 
     For query i in block b:
-      exact logits   s_j = scale * q_i . k_j            for every key j in E_b's blocks
+      exact logits   s_j = scale * q_i . k_j            for every key j in E_b's key blocks
       cluster logits t_c = scale * q_i . mu_c + ln n[b][c]   for every c with n[b][c] > 0
       o_i   = (sum_j e^{s_j - m} v_j + sum_c e^{t_c - m} vbar_c) / (sum of the same weights)
       lse_i = m + ln(sum of weights), m = the largest logit.
@@ -216,7 +227,7 @@ def forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mu: np.ndarray, vbar: n
     for b in (range(nb) if qblocks is None else qblocks):
         rows = slice(b * block, min(n_tok, (b + 1) * block))
         q = Q[rows]
-        ex = _exact_keys(mask[b], block, n_tok)
+        ex = _exact_keys(mask[b], block if kblock is None else kblock, n_tok)
         cs = np.nonzero(counts[b] > 0)[0]
         logits = np.concatenate(
             [scale * (q @ K[ex].T),
@@ -233,8 +244,9 @@ def forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mu: np.ndarray, vbar: n
 
 def forward_substituted(Q: np.ndarray, K: np.ndarray, V: np.ndarray, a: np.ndarray,
                         mu: np.ndarray, vbar: np.ndarray, mask: np.ndarray, block: int,
-                        scale: Optional[float] = None) -> np.ndarray:
-    """Brute force for tiny inputs: for query block b, every key outside E_b's blocks is
+                        scale: Optional[float] = None, kblock: Optional[int] = None
+                        ) -> np.ndarray:
+    """Brute force for tiny inputs: for query block b, every key outside E_b's key blocks is
     replaced by its cluster's centroid key and mean value, then plain softmax attention
     runs over all N (substituted) keys. Same quantity as `forward`, built per key."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
@@ -242,12 +254,13 @@ def forward_substituted(Q: np.ndarray, K: np.ndarray, V: np.ndarray, a: np.ndarr
     n_tok, d = Q.shape
     scale = default_scale(d) if scale is None else scale
     O = np.empty((n_tok, d))
+    kb_size = block if kblock is None else kblock
     for i in range(n_tok):
         b = i // block
         Kt = np.empty_like(K)
         Vt = np.empty_like(V)
         for j in range(n_tok):
-            if mask[b][j // block]:
+            if mask[b][j // kb_size]:
                 Kt[j], Vt[j] = K[j], V[j]
             else:
                 Kt[j], Vt[j] = mu[a[j]], vbar[a[j]]

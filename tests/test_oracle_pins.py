@@ -293,3 +293,87 @@ def test_bf16_cache_refresh_rounds_means():
     np.testing.assert_array_equal(st["mu1"], O.storage_round(st["mu1_exact"], "bf16"))
     assert np.max(np.abs(st["mu1"] - st["mu1_exact"]) / np.maximum(
         np.abs(st["mu1_exact"]), 1e-30)) <= 2 ** -8
+
+
+# ----------------------------------------------------------------- key blocks finer than query blocks
+def test_hand_worked_key_blocks():
+    """Exact keys chosen one at a time (key block S = 1 inside query blocks of 2): counts
+    and outputs against closed forms worked on paper."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_key_blocks.json")))
+    e = g["expected"]
+    B, S, scale = g["block"], g["key_block"], g["scale"]
+    mask = np.array(g["mask"], np.uint8)
+    K = np.log(np.array(g["x_of_keys"], float))[:, None]
+    Q = np.array(g["q"], float)[:, None]
+    V = np.array(g["v"], float)[:, None]
+    mu0 = np.array(g["mu0"], float)[:, None]
+    st = O.reassign_step(K, V, mu0, mask, B, "f64", kblock=S)
+    assert st["counts"].tolist() == e["counts"]
+    out, lse = O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], mask, B, scale=scale,
+                         kblock=S)
+    den = np.array(e["out_den"], float)
+    np.testing.assert_allclose(out[:, 0], np.array(e["out_num"], float) / den, rtol=1e-13)
+    np.testing.assert_allclose(lse, np.log(den), rtol=1e-13)
+    sub = O.forward_substituted(Q, K, V, st["assign"], st["mu1"], st["vbar"], mask, B,
+                                scale=scale, kblock=S)
+    np.testing.assert_allclose(sub[:, 0], np.array(e["out_num"], float) / den, rtol=1e-13)
+
+
+def _expand(mask, factor, n_keys_blocks):
+    """Block mask [nb][nb] -> the same exact key set at key blocks `factor` times finer."""
+    return np.repeat(mask, factor, axis=1)[:, :n_keys_blocks]
+
+
+@pytest.mark.parametrize("S", [16, 32])
+def test_expanded_mask_is_the_block_mask(S):
+    """A key-block mask that keeps exactly the keys of a query-sized block mask gives the
+    same counts and the same forward, to the last bit (same exact key set, same order)."""
+    n, d, B, C = 300, 16, 64, 7
+    Q, K, V = _rand(60, n, d), _rand(61, n, d), _rand(62, n, d)
+    nb = -(-n // B)
+    m = _mask(63, nb, 0.4)
+    ms = _expand(m, B // S, -(-n // S))
+    mu0 = K[::40][:C].copy()
+    st = O.reassign_step(K, V, mu0, m, B, "f64")
+    ss = O.reassign_step(K, V, mu0, ms, B, "f64", kblock=S)
+    np.testing.assert_array_equal(st["counts"], ss["counts"])
+    o1, l1 = O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], m, B)
+    o2, l2 = O.forward(Q, K, V, ss["mu1"], ss["vbar"], ss["counts"], ms, B, kblock=S)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("seed", [70, 71])
+def test_key_blocks_match_substitution_brute_force(seed):
+    """Key blocks of 8 inside query blocks of 32, ragged at both granularities (N = 150):
+    the count-weighted forward equals attention over all keys with every key outside the
+    exact key blocks replaced by its cluster's centroid and mean value."""
+    n, d, B, S, C = 150, 8, 32, 8, 6
+    Q, K, V = _rand(seed, n, d), _rand(seed + 1, n, d), _rand(seed + 2, n, d)
+    nb, nkb = -(-n // B), -(-n // S)
+    mask = (np.random.default_rng(seed + 3).random((nb, nkb)) < 0.3).astype(np.uint8)
+    st = O.reassign_step(K, V, K[::25][:C].copy(), mask, B, "f64", kblock=S)
+    out, _ = O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], mask, B, kblock=S)
+    sub = O.forward_substituted(Q, K, V, st["assign"], st["mu1"], st["vbar"], mask, B,
+                                kblock=S)
+    np.testing.assert_allclose(out, sub, rtol=1e-12, atol=1e-13)
+
+
+def test_key_block_count_invariants():
+    """Counts at key-block granularity: sum_c n[b][c] is N minus the valid keys of b's
+    exact key blocks (the last one ragged), and n = N_c minus a key-by-key histogram."""
+    n, d, B, S, C = 333, 8, 64, 16, 11
+    K, V = _rand(80, n, d), _rand(81, n, d)
+    nb, nkb = -(-n // B), -(-n // S)
+    mask = (np.random.default_rng(82).random((nb, nkb)) < 0.35).astype(np.uint8)
+    mask[:, nkb - 1] = 1                      # every query block keeps the ragged key block
+    st = O.reassign_step(K, V, K[::30][:C].copy(), mask, B, "f64", kblock=S)
+    a, sizes, cnt = st["assign"], st["sizes"], st["counts"]
+    for b in range(nb):
+        valid = sum(min(n, (kb + 1) * S) - kb * S for kb in range(nkb) if mask[b, kb])
+        assert cnt[b].sum() == n - valid
+        inside = np.zeros(C, np.int64)
+        for j in range(n):
+            if mask[b, j // S]:
+                inside[a[j]] += 1
+        np.testing.assert_array_equal(cnt[b], sizes - inside)
