@@ -15,9 +15,11 @@ Streams: 0 centres, 1 K components, 2 K noise, 3 Q components, 4 Q noise, 5 V,
 
 The mask is a plan input: position-fixed exact key blocks per query block. Three kinds:
   * "random": the diagonal block plus (k - 1) distinct seeded other blocks per row;
-  * "local": the k key blocks nearest in a 3D sense, distance^2 between block centres
-    (S*df)^2 + dr^2 + dw^2 with S = Hs / 4, ties to the smaller block index; optionally
-    every block holding a token of frame 0 is kept first ("first-frame" blocks);
+  * "local": the k key blocks nearest in a 3D sense, distance^2 between the query block's
+    centre and the key block's centre (S*df)^2 + dr^2 + dw^2 with S = Hs / 4, ties to the
+    smaller block index; optionally every key block holding a token of frame 0 is kept
+    first ("first-frame" blocks). Key blocks may be smaller than query blocks
+    (`key_block`); k then counts key blocks of that size;
   * "local_budget": the same nearest-block rule with a budget k[h][b] per head and query
     block (one mask per head). Budgets are k times a head factor and a block factor, each
     log-uniform in [1/2, 2] and seeded per head, rescaled so their mean over the layer is
@@ -61,6 +63,7 @@ class LayerConfig:
     drift_v: bool
     drift_sigma: float = 0.05
     description: str = ""
+    key_block: int = 0      # exact key block size (0: the query block size)
 
     @property
     def seq_len(self) -> int:
@@ -69,6 +72,14 @@ class LayerConfig:
     @property
     def num_blocks(self) -> int:
         return -(-self.seq_len // self.block)
+
+    @property
+    def kblock(self) -> int:
+        return self.key_block or self.block
+
+    @property
+    def num_key_blocks(self) -> int:
+        return -(-self.seq_len // self.kblock)
 
     @property
     def local_scale(self) -> float:
@@ -116,6 +127,41 @@ CONFIGS: Dict[str, LayerConfig] = {
         drift_v=False,
         description="13B-class layer with per-head and per-block budgets averaging 46 of "
                     "929 key blocks (5% density), one 3D-local mask per head"),
+    "small_sub32_bf16": LayerConfig(
+        "small_sub32_bf16", 8, heads=4, frames=8, height=32, width=32, head_dim=128,
+        block=128, clusters=128, mask_kind="local", blocks_per_row=48, first_frame=False,
+        mixture=64, sigma=0.3, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_block=32,
+        description="4 heads, N=8192 (8x32x32), d=128, query blocks of 128, exact key blocks "
+                    "of 32: the 48 nearest per query block (18.75%, 3D-local)"),
+    "small_sub16_d64_bf16": LayerConfig(
+        "small_sub16_d64_bf16", 9, heads=3, frames=3, height=30, width=30, head_dim=64,
+        block=128, clusters=64, mask_kind="local", blocks_per_row=48, first_frame=True,
+        mixture=64, sigma=0.3, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_block=16,
+        description="3 heads, N=2700 (3x30x30, ragged at both block sizes), d=64, query "
+                    "blocks of 128, exact key blocks of 16: first frame + nearest, 48 per "
+                    "query block"),
+    "tiny_sub_f32": LayerConfig(
+        "tiny_sub_f32", 10, heads=1, frames=4, height=15, width=17, head_dim=64, block=64,
+        clusters=16, mask_kind="local", blocks_per_row=16, first_frame=False, mixture=16,
+        sigma=0.3, dtype="f32", steps=0, drift_k=False, drift_v=False, key_block=16,
+        description="1 head, N=1020 (4x15x17), d=64, query blocks of 64, exact key blocks of "
+                    "16 (16 nearest per query block), fp32"),
+    "hunyuan13b_sub32_bf16": LayerConfig(
+        "hunyuan13b_sub32_bf16", 11, heads=24, frames=33, height=45, width=80, head_dim=128,
+        block=128, clusters=512, mask_kind="local", blocks_per_row=184, first_frame=False,
+        mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_block=32,
+        description="13B-class layer with exact key blocks of 32 keys: the 184 nearest per "
+                    "query block of 128, the same 5% of keys as 46 blocks of 128"),
+    "hunyuan13b_sub64_bf16": LayerConfig(
+        "hunyuan13b_sub64_bf16", 12, heads=24, frames=33, height=45, width=80, head_dim=128,
+        block=128, clusters=512, mask_kind="local", blocks_per_row=92, first_frame=False,
+        mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_block=64,
+        description="13B-class layer with exact key blocks of 64 keys: the 92 nearest per "
+                    "query block of 128 (5% of keys)"),
     "extreme_cache_bf16": LayerConfig(
         "extreme_cache_bf16", 5, heads=40, frames=21, height=45, width=80, head_dim=128,
         block=128, clusters=512, mask_kind="local", blocks_per_row=6, first_frame=False,
@@ -193,11 +239,13 @@ def apply_drift(cfg: LayerConfig, stored: np.ndarray, head: int, step: int,
 
 
 # ---------------------------------------------------------------- masks
-def _block_centres(cfg: LayerConfig) -> np.ndarray:
-    n, b, hw, w = cfg.seq_len, cfg.block, cfg.height * cfg.width, cfg.width
+def _block_centres(cfg: LayerConfig, size: Optional[int] = None) -> np.ndarray:
+    """Mean (frame, row, column) of the tokens of each block of `size` tokens."""
+    n, hw, w = cfg.seq_len, cfg.height * cfg.width, cfg.width
+    b = cfg.block if size is None else size
     t = np.arange(n, dtype=np.int64)
     coords = np.stack([t // hw, (t // w) % cfg.height, t % w], axis=1).astype(np.float64)
-    nb = cfg.num_blocks
+    nb = -(-n // b)
     cen = np.zeros((nb, 3))
     for kb in range(nb):
         cen[kb] = coords[kb * b:min(n, (kb + 1) * b)].mean(axis=0)
@@ -231,10 +279,12 @@ def _local_orders(cfg: LayerConfig) -> np.ndarray:
 
 
 def block_mask(cfg: LayerConfig) -> np.ndarray:
-    """uint8 [1][nb][nb] (or [H][nb][nb] for per-head budgets); nonzero = key block computed
+    """uint8 [1][nb][nkb] (or [H][nb][nb] for per-head budgets); nonzero = key block computed
     exactly for that query block."""
     nb, k = cfg.num_blocks, cfg.blocks_per_row
-    if not 1 <= k <= nb:
+    if cfg.kblock != cfg.block and cfg.mask_kind != "local":
+        raise ValueError("key blocks smaller than query blocks need a local mask")
+    if not 1 <= k <= cfg.num_key_blocks:
         raise ValueError("blocks_per_row out of range")
     if cfg.mask_kind == "local_budget":
         kk = budgets(cfg)
@@ -255,15 +305,18 @@ def block_mask(cfg: LayerConfig) -> np.ndarray:
         return mask[None]
     if cfg.mask_kind != "local":
         raise ValueError(cfg.mask_kind)
-    cen = _block_centres(cfg)
+    nkb = cfg.num_key_blocks
+    mask = np.zeros((nb, nkb), dtype=np.uint8)
+    cen_q = _block_centres(cfg)
+    cen = _block_centres(cfg, cfg.kblock)
     s = cfg.local_scale
-    forced = np.zeros(nb, dtype=bool)
+    forced = np.zeros(nkb, dtype=bool)
     if cfg.first_frame:
         hw = cfg.height * cfg.width
-        forced[: (min(hw, cfg.seq_len) - 1) // cfg.block + 1] = True
-    idx = np.arange(nb)
+        forced[: (min(hw, cfg.seq_len) - 1) // cfg.kblock + 1] = True
+    idx = np.arange(nkb)
     for b in range(nb):
-        diff = cen - cen[b]
+        diff = cen - cen_q[b]
         dist2 = (s * diff[:, 0]) ** 2 + diff[:, 1] ** 2 + diff[:, 2] ** 2
         order = np.lexsort((idx, dist2))          # by distance, then by block index
         chosen = list(idx[forced][:k])

@@ -19,6 +19,7 @@
  *       assign               [H][N]      int32
  *       cluster_sizes        [H][C]      int32
  *       qblock_counts        [H][nb][C]  int32, nb = ceil(N / block)
+ *       block mask (host)    [mask_heads][nb][nkb] uint8, nkb = ceil(N / key_block)
  *       lse                  [H][N]      float (natural-log log-sum-exp of each row)
  *     N need not be a multiple of the block size; exactly N rows are read and written.
  *   - Device pointers to element tensors must be 16-byte aligned; int32/float outputs
@@ -61,11 +62,17 @@ typedef enum { DA_DTYPE_F32 = 0, DA_DTYPE_BF16 = 1 } da_dtype;
  *   heads       H >= 1
  *   seq_len     N >= 1 tokens per head
  *   head_dim    d in {64, 128}
- *   block       B in {64, 128}: query and key block size of the mask
+ *   block       B in {64, 128}: query block size of the mask (and the tile height)
  *   clusters    C, 1 <= C <= N and C <= 8192
  *   mask_heads  1 (one mask shared by all heads) or H (one mask per head)
  *   dtype       element type of Q, K, V, O and the cluster cache (da_dtype)
- *   scale       softmax scale; 0 selects 1/sqrt(d). Must be finite and >= 0. */
+ *   scale       softmax scale; 0 selects 1/sqrt(d). Must be finite and >= 0.
+ *   key_block   S, the size of the exact key blocks; 0 selects S = B. S in {16, 32, 64,
+ *               128} with S <= B. With S < B the forward packs B/S exact key blocks of a
+ *               query block into each B-row tile (Accurate Block Attention (AB-Attention),
+ *               Abstract: key/value blocks smaller than a tile gathered into full
+ *               tensor-core tiles), so exact keys are chosen at the finer granularity for
+ *               the matrix-core cost of B-row tiles. */
 typedef struct {
   int32_t heads;
   int32_t seq_len;
@@ -75,6 +82,7 @@ typedef struct {
   int32_t mask_heads;
   int32_t dtype;
   float scale;
+  int32_t key_block;
 } da_desc;
 
 typedef struct da_plan_s* da_plan;
@@ -82,9 +90,10 @@ typedef struct da_plan_s* da_plan;
 /* Compile a plan from a position-fixed block mask (abstract: the exact blocks are fixed
  * once offline by position; one plan is compiled offline and reused every step).
  *   desc             layer shape (copied).
- *   block_mask_host  HOST array uint8 [mask_heads][nb][nb]; nonzero at [h][b][kb] means
- *                    key block kb is attended exactly by query block b. Any pattern is
- *                    legal, including rows with no exact block. Copied; not retained.
+ *   block_mask_host  HOST array uint8 [mask_heads][nb][nkb]; nonzero at [h][b][kb] means
+ *                    key block kb (keys kb*S .. min(N, (kb+1)*S) - 1) is attended exactly
+ *                    by query block b. Any pattern is legal, including rows with no exact
+ *                    block. Copied; not retained.
  *   out              receives the plan handle (set to NULL on error).
  * Builds the per-query-block exact lists (sorted key-block indices), uploads them and
  * allocates the reassignment workspace. This is the only call that allocates device
@@ -107,7 +116,7 @@ DA_API da_status da_plan_destroy(da_plan plan);
  *                      stored values, fp32 accumulation; exact ties go to the lowest c).
  *   cluster_sizes_out  [H][C] number of keys per cluster.
  *   qblock_counts_out  [H][nb][C] n[b][c]: keys of cluster c outside query block b's
- *                      exact key blocks.
+ *                      exact key blocks (counted key by key, whatever the key block size).
  * All outputs are written in full. Errors: INVALID_ARGUMENT, DEVICE. */
 DA_API da_status da_reassign(da_plan plan, const void* K, const void* V,
                              const void* centroids_in, void* centroids_out,
@@ -136,12 +145,14 @@ DA_API da_status da_forward(da_plan plan, const void* Q, const void* K, const vo
 /* Plan introspection (host-side values; no device work).
  *   num_blocks       nb = ceil(N / block)
  *   exact_pairs      total number of (query block, exact key block) pairs over mask heads
+ *                    (key blocks of the plan's key block size)
  *   workspace_bytes  device bytes the plan owns (exact lists + reassignment workspace) */
 DA_API da_status da_plan_info(da_plan plan, int32_t* num_blocks, int64_t* exact_pairs,
                               int64_t* workspace_bytes);
 
 /* Copy of the plan's exact lists for mask head mh: rowptr[nb+1] and col[rowptr[nb]]
- * (sorted key-block indices per query block). Either output may be NULL to skip it. */
+ * (sorted key-block indices, in key blocks of the plan's key block size, per query block).
+ * Either output may be NULL to skip it. */
 DA_API da_status da_plan_exact_lists(da_plan plan, int32_t mh, int32_t* rowptr,
                                      int32_t* col);
 

@@ -29,7 +29,8 @@ class da_desc(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("clusters", ctypes.c_int32), ("mask_heads", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("key_block", ctypes.c_int32)]
 
 
 class DAError(RuntimeError):
@@ -85,9 +86,11 @@ def da_version() -> int:
 
 
 def make_desc(heads: int, seq_len: int, head_dim: int, block: int, clusters: int,
-              dtype: str = "bf16", mask_heads: int = 1, scale: float = 0.0) -> da_desc:
+              dtype: str = "bf16", mask_heads: int = 1, scale: float = 0.0,
+              key_block: int = 0) -> da_desc:
     return da_desc(heads, seq_len, head_dim, block, clusters, mask_heads,
-                   DTYPES.get(dtype, dtype) if isinstance(dtype, str) else int(dtype), scale)
+                   DTYPES.get(dtype, dtype) if isinstance(dtype, str) else int(dtype), scale,
+                   key_block)
 
 
 def _mask_ptr(mask: Optional[np.ndarray]):
@@ -137,24 +140,31 @@ def _ptr(t) -> Optional[int]:
 
 
 class Plan:
-    """A compiled plan: fixed exact key blocks per query block plus device workspace."""
+    """A compiled plan: fixed exact key blocks per query block plus device workspace.
+
+    `mask` is [mask_heads][nb][nkb] (or [nb][nkb]) with nb = ceil(N / block) query blocks
+    and nkb = ceil(N / key_block) key blocks; key_block None or 0 means key_block = block."""
 
     def __init__(self, heads: int, seq_len: int, head_dim: int, block: int, clusters: int,
-                 mask: np.ndarray, dtype: str = "bf16", scale: float = 0.0):
+                 mask: np.ndarray, dtype: str = "bf16", scale: float = 0.0,
+                 key_block: Optional[int] = None):
         mask = np.asarray(mask, dtype=np.uint8)
         if mask.ndim == 2:
             mask = mask[None]
+        kblock = int(key_block or 0)
         self.desc = make_desc(heads, seq_len, head_dim, block, clusters, dtype,
-                              mask_heads=mask.shape[0], scale=scale)
+                              mask_heads=mask.shape[0], scale=scale, key_block=kblock)
         nb = -(-seq_len // block)
-        if mask.shape[1:] != (nb, nb):
-            raise ValueError(f"mask must be [mask_heads][{nb}][{nb}], got {mask.shape}")
+        nkb = -(-seq_len // (kblock or block))
+        if mask.shape[1:] != (nb, nkb):
+            raise ValueError(f"mask must be [mask_heads][{nb}][{nkb}], got {mask.shape}")
         st, h = da_plan_create(self.desc, mask)
         if st != DA_OK:
             raise DAError(st, "da_plan_create")
         self._h = h
         self.heads, self.seq_len, self.head_dim = heads, seq_len, head_dim
         self.block, self.clusters, self.dtype, self.num_blocks = block, clusters, dtype, nb
+        self.key_block, self.num_key_blocks = kblock or block, nkb
 
     # -- introspection
     def info(self) -> Dict[str, int]:

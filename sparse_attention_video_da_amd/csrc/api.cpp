@@ -20,11 +20,13 @@ hipError_t prepare_reassign_kernels();
 struct da_plan_s {
   da_desc desc;
   int32_t nb;
+  int32_t kblock;               // exact key block size S
+  int32_t nkb;                  // ceil(N / S)
   float scale;
   std::vector<int32_t> rowptr;  // [mask_heads][nb + 1], absolute offsets into col
   std::vector<int32_t> col;
-  // query-block pairs (2p, 2p+1): ascending union of both exact lists, each entry
-  // kb | (kb exact for 2p) << 28 | (kb exact for 2p+1) << 29
+  // query-block pairs (2p, 2p+1): union of both exact lists in the da::kEnt* entry format
+  // (ascending when S = B; grouped by user and padded to a multiple of B/S when S < B)
   std::vector<int32_t> prowptr;  // [mask_heads][npairs + 1]
   std::vector<int32_t> pcol;
   int32_t npairs = 0;
@@ -54,6 +56,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t elem_size(const da_desc& d) { return d.dtype == DA_DTYPE_BF16 ? 2 : 4; }
 
+int32_t key_block_of(const da_desc& d) { return d.key_block > 0 ? d.key_block : d.block; }
+
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
@@ -70,10 +74,14 @@ da_status check_desc(const da_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return DA_ERR_UNSUPPORTED;
   if (d->block != 64 && d->block != 128) return DA_ERR_UNSUPPORTED;
   if (d->clusters > kMaxClusters) return DA_ERR_UNSUPPORTED;
-  // int32 indexing of [H][N][d] element offsets and [H][nb][C] counts
+  if (d->key_block < 0) return DA_ERR_INVALID_ARGUMENT;
+  const int32_t S = key_block_of(*d);
+  if ((S != 16 && S != 32 && S != 64 && S != 128) || S > d->block) return DA_ERR_UNSUPPORTED;
+  // int32 indexing of [H][N][d] element offsets, [H][nb][C] counts and the mask
   const int64_t nb = (d->seq_len + d->block - 1) / d->block;
+  const int64_t nkb = (d->seq_len + S - 1) / S;
   if ((int64_t)d->seq_len * d->head_dim > INT32_MAX || nb * d->clusters > INT32_MAX ||
-      nb * nb * d->mask_heads > INT32_MAX)
+      nb * nkb * d->mask_heads > INT32_MAX)
     return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
@@ -106,7 +114,7 @@ DA_API const char* da_status_str(da_status s) {
   return "unknown status";
 }
 
-DA_API int32_t da_version(void) { return 100; }
+DA_API int32_t da_version(void) { return 101; }
 
 DA_API da_status da_validate_desc(const da_desc* desc, const uint8_t* mask) {
   const da_status st = check_desc(desc);
@@ -125,38 +133,61 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
   if (p == nullptr) return DA_ERR_OUT_OF_MEMORY;
   p->desc = *desc;
   const int32_t nb = (desc->seq_len + desc->block - 1) / desc->block;
+  const int32_t S = key_block_of(*desc);
+  const int32_t nkb = (desc->seq_len + S - 1) / S;
+  const int32_t G = desc->block / S;   // exact key blocks per B-row tile
   p->nb = nb;
+  p->kblock = S;
+  p->nkb = nkb;
   p->scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt((float)desc->head_dim);
   // Exact lists: for each mask head and query block, the ascending key blocks kept exact.
   p->rowptr.resize((size_t)desc->mask_heads * (nb + 1));
   for (int32_t mh = 0; mh < desc->mask_heads; ++mh) {
-    const uint8_t* m = mask + (size_t)mh * nb * nb;
+    const uint8_t* m = mask + (size_t)mh * nb * nkb;
     for (int32_t b = 0; b < nb; ++b) {
       p->rowptr[(size_t)mh * (nb + 1) + b] = (int32_t)p->col.size();
-      for (int32_t kb = 0; kb < nb; ++kb)
-        if (m[(size_t)b * nb + kb]) p->col.push_back(kb);
+      for (int32_t kb = 0; kb < nkb; ++kb)
+        if (m[(size_t)b * nkb + kb]) p->col.push_back(kb);
     }
     p->rowptr[(size_t)mh * (nb + 1) + nb] = (int32_t)p->col.size();
   }
+  // Pair lists. With several key blocks per tile, the blocks both query blocks use come
+  // first and those of one query block after, so a tile mixes users at most at the two
+  // seams and a query block's waves skip the tiles that hold none of its keys.
   const int32_t npairs = (nb + 1) / 2;
+  const bool partial_last = desc->seq_len % S != 0;
   p->npairs = npairs;
   p->prowptr.resize((size_t)desc->mask_heads * (npairs + 1));
+  std::vector<int32_t> only0, only1;
   for (int32_t mh = 0; mh < desc->mask_heads; ++mh) {
-    const uint8_t* m = mask + (size_t)mh * nb * nb;
+    const uint8_t* m = mask + (size_t)mh * nb * nkb;
     for (int32_t pr = 0; pr < npairs; ++pr) {
       p->prowptr[(size_t)mh * (npairs + 1) + pr] = (int32_t)p->pcol.size();
       const int32_t b0 = 2 * pr, b1 = 2 * pr + 1;
-      for (int32_t kb = 0; kb < nb; ++kb) {
-        const int32_t f0 = m[(size_t)b0 * nb + kb] ? 1 : 0;
-        const int32_t f1 = (b1 < nb && m[(size_t)b1 * nb + kb]) ? 1 : 0;
-        if (f0 | f1) p->pcol.push_back(kb | (f0 << 28) | (f1 << 29));
+      only0.clear();
+      only1.clear();
+      for (int32_t kb = 0; kb < nkb; ++kb) {
+        const int32_t f0 = m[(size_t)b0 * nkb + kb] ? 1 : 0;
+        const int32_t f1 = (b1 < nb && m[(size_t)b1 * nkb + kb]) ? 1 : 0;
+        if (!(f0 | f1)) continue;
+        const int32_t ent = kb | (f0 << da::kEntUse0) | (f1 << da::kEntUse1) |
+                            ((partial_last && kb == nkb - 1) ? 1 << da::kEntPartial : 0);
+        if (G == 1 || (f0 & f1)) p->pcol.push_back(ent);
+        else (f0 ? only0 : only1).push_back(ent);
+      }
+      p->pcol.insert(p->pcol.end(), only0.begin(), only0.end());
+      p->pcol.insert(p->pcol.end(), only1.begin(), only1.end());
+      const int32_t len = (int32_t)p->pcol.size() - p->prowptr[(size_t)mh * (npairs + 1) + pr];
+      if (G > 1 && len % G != 0) {
+        const int32_t pad = p->pcol.back() & ~((1 << da::kEntUse0) | (1 << da::kEntUse1));
+        for (int32_t i = len % G; i < G; ++i) p->pcol.push_back(pad);
       }
     }
     p->prowptr[(size_t)mh * (npairs + 1) + npairs] = (int32_t)p->pcol.size();
   }
   // Balanced split of the forward's work items over the 8 XCDs (workgroup ids are dealt to
-  // XCDs round-robin). An item's work is its tile count: the union of the pair's exact
-  // lists plus the cluster tiles, plus one tile for its prologue and epilogue. Contiguous
+  // XCDs round-robin). An item's work is its tile count: the exact tiles of the pair's
+  // union list plus the cluster tiles, plus one tile for its prologue and epilogue. Contiguous
   // ranges keep neighbouring query blocks, which share key blocks, on one L2; equal work
   // per range keeps the XCDs busy equally long when budgets differ across heads or blocks.
   {
@@ -166,7 +197,7 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
     for (int64_t i = 0; i < items; ++i) {
       const int32_t h = (int32_t)(i / npairs), pr = (int32_t)(i % npairs);
       const size_t base = (size_t)(desc->mask_heads == 1 ? 0 : h) * (npairs + 1);
-      const int64_t len = p->prowptr[base + pr + 1] - p->prowptr[base + pr];
+      const int64_t len = (p->prowptr[base + pr + 1] - p->prowptr[base + pr]) / G;
       pre[(size_t)i + 1] = pre[(size_t)i] + len + ctiles + 1;
     }
     int64_t at = 0;
@@ -304,6 +335,7 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
   a.nb = p->nb;
   a.block = d.block;
   a.mask_heads = d.mask_heads;
+  a.kblock = p->kblock;
   const hipError_t e = da::launch_reassign(a, d.head_dim, d.dtype == DA_DTYPE_BF16,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;
@@ -342,8 +374,10 @@ DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void*
   a.C = d.clusters;
   a.nb = p->nb;
   a.mask_heads = d.mask_heads;
+  a.kblock = p->kblock;
   a.scale_log2e = p->scale * 1.4426950408889634f;
-  const hipError_t e = da::launch_forward(a, d.head_dim, d.block, d.dtype == DA_DTYPE_BF16,
+  const hipError_t e = da::launch_forward(a, d.head_dim, d.block, p->kblock,
+                                          d.dtype == DA_DTYPE_BF16,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;
 }

@@ -6,6 +6,13 @@
 
 namespace da {
 
+// Pair-list entry: key block index | used by query block 2p | used by 2p+1 | the key block
+// runs past N. With B/S key blocks per tile (S < B) a pair's list holds the blocks both
+// query blocks use, then those only 2p uses, then those only 2p+1 uses (each ascending), and
+// is padded to a multiple of B/S with copies of its last entry whose use bits are clear.
+constexpr int32_t kEntIndex = 0x0fffffff;
+constexpr int kEntUse0 = 28, kEntUse1 = 29, kEntPartial = 30;
+
 // Everything the fused forward kernel reads, in device memory.
 struct FwdArgs {
   const void* Q;
@@ -15,15 +22,16 @@ struct FwdArgs {
   const void* vbar;      // [H][C][d] mean values
   const int32_t* counts; // [H][nb][C]
   const int32_t* rowptr; // [mask_heads][nb + 1], absolute offsets into col
-  const int32_t* col;    // sorted exact key blocks
+  const int32_t* col;    // sorted exact key blocks (of kblock keys)
   const int32_t* prowptr; // [mask_heads][npairs + 1] lists of query-block pairs (2p, 2p+1)
-  const int32_t* pcol;    // union of the pair's exact blocks: kb | (in 2p) << 28 | (in 2p+1) << 29
+  const int32_t* pcol;    // union of the pair's exact key blocks (entry format: kEnt* above)
   int npairs;
   int xstart[9];         // items (h * npairs + pair) xstart[x] .. xstart[x+1]-1 run on XCD x
   int xmax;              // largest range
   void* O;
   float* lse;            // may be null
   int H, N, C, nb, mask_heads;
+  int kblock;            // exact key block size S (divides the query block size)
   float scale_log2e;     // softmax scale * log2(e)
 };
 
@@ -48,10 +56,11 @@ struct ReassignArgs {
   uint16_t* cop;   // workspace: bf16 distance operands, [H][C][D] (-2 mu) then [H][C][8]
   float* part;     // workspace [H][ceil(N / 256) + C][2][D] partial sums of K and V
   int H, N, C, nb, block, mask_heads;
+  int kblock;      // exact key block size S
 };
 
 // Return hipSuccess or the first launch error.
-hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, bool bf16,
+hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, int kblock, bool bf16,
                           hipStream_t stream);
 hipError_t launch_reassign(const ReassignArgs& a, int head_dim, bool bf16, hipStream_t stream);
 // One-time per-process kernel attribute setup (dynamic LDS limits).

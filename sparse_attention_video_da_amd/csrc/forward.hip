@@ -1,7 +1,8 @@
 // Fused decoupled sparse attention forward for gfx950.
 //
-// A workgroup walks exact key blocks (the plan's sorted lists) and then the cluster-cache
-// tiles (C centroid keys / mean values taken BLK at a time), treating both the same way:
+// A workgroup walks exact tiles (BLK keys: one key block of BLK keys, or BLK/S key blocks
+// of S keys gathered from anywhere in K and V) and then the cluster-cache tiles (C centroid
+// keys / mean values taken BLK at a time), treating both the same way:
 // the tile's keys and values are staged in LDS, scores come from MFMA, and a single online
 // softmax (exp2 domain) absorbs every tile. Cluster tiles add a per-key logit bias
 // log2(n[b][c]) (-inf where n = 0), which in the natural-log domain is the ln-count weight
@@ -32,16 +33,20 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
 
 // ----------------------------------------------------------------------------- bf16
 // A workgroup owns two adjacent query blocks (2p, 2p+1) of one head: BLK/32 waves per
-// block. It walks the ascending union of the two exact lists, so a key block both blocks
-// keep exact is fetched once (neighbouring query blocks of a 3D-local mask share most of
-// their key blocks), then the cluster tiles, which both blocks use with their own bias
-// rows. A wave skips the tiles its block does not keep.
+// block. It walks the union of the two exact lists, so a key block both blocks keep exact
+// is fetched once (neighbouring query blocks of a 3D-local mask share most of their key
+// blocks), then the cluster tiles, which both blocks use with their own bias rows. An
+// exact tile holds G = BLK/S consecutive list entries; with G > 1 the list puts the key
+// blocks both query blocks use first, so nearly every tile serves one set of users. A wave
+// skips the tiles that hold no key of its block, and the bias row of the tile masks the
+// key blocks of a mixed tile that its block does not keep.
 struct TileDesc {
-  int off;         // byte offset of the tile's first row in K and V, or in the cache arrays
-  int valid;       // rows that exist (keys < N, or clusters < C)
-  int kind;        // 0 full exact block, 1 ragged exact block, 2 cluster tile
+  int off;         // cluster tile: byte offset of its first row in the cache arrays
+  int valid;       // cluster tile: rows that exist (clusters < C)
+  int kind;        // 0 exact tile, 2 cluster tile
   int c0;          // first cluster of a cluster tile
-  int use;         // bit h: query block 2p+h uses this tile
+  int use;         // bit h: query block 2p+h uses some key of this tile
+  int partial;     // exact tile: one of its key blocks runs past N
 };
 
 // Read-only, wave-uniform loads through the scalar cache.
@@ -49,23 +54,36 @@ __device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
   return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
 }
 
-template <int D, int BLK>
-__device__ __forceinline__ TileDesc tile_desc(int t, int n_list, int entry, int N, int C) {
+// en[first + j] for a per-lane j in [0, R): a chain of selects over scalar registers.
+template <int R, int G>
+__device__ __forceinline__ int pick(const int (&en)[G], int first, int j) {
+  int v = en[first];
+#pragma unroll
+  for (int i = 1; i < R; ++i) v = j == i ? en[first + i] : v;
+  return v;
+}
+
+template <int D, int BLK, int G>
+__device__ __forceinline__ TileDesc tile_desc(int t, int n_ex, const int (&en)[G], int C) {
   TileDesc d;
-  if (t < n_list) {
-    const int kb = entry & 0x0fffffff;
-    d.off = kb * BLK * D * 2;
-    d.valid = min(BLK, N - kb * BLK);
-    d.kind = d.valid < BLK ? 1 : 0;
+  if (t < n_ex) {
+    int u = 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) u |= en[j];
+    d.off = 0;
+    d.valid = BLK;
+    d.kind = 0;
     d.c0 = 0;
-    d.use = (entry >> 28) & 3;
+    d.use = (u >> kEntUse0) & 3;
+    d.partial = (u >> kEntPartial) & 1;
   } else {
-    const int ct = t - n_list;
+    const int ct = t - n_ex;
     d.c0 = ct * BLK;
     d.off = d.c0 * D * 2;
     d.valid = min(BLK, C - d.c0);
     d.kind = 2;
     d.use = 3;
+    d.partial = 0;
   }
   return d;
 }
@@ -84,9 +102,11 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
-template <int D, int BLK>
+template <int D, int BLK, int S>
 __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdArgs p) {
+  constexpr int G = BLK / S;       // exact key blocks per tile
+  static_assert(G * S == BLK && S >= 16, "key blocks must tile the query block");
   constexpr int THREADS = BLK * 4;
   constexpr int WPB = BLK / 32;    // waves per query block
   constexpr int KT = BLK / 32;     // 32-key subtiles per key block
@@ -153,8 +173,8 @@ fwd_bf16_kernel(FwdArgs p) {
 
   const int mh = p.mask_heads == 1 ? 0 : h;
   const int e0 = sload(p.prowptr, mh * (p.npairs + 1) + pr);
-  const int n_list = sload(p.prowptr, mh * (p.npairs + 1) + pr + 1) - e0;
-  const int ntiles = n_list + (p.C + BLK - 1) / BLK;
+  const int n_ex = (sload(p.prowptr, mh * (p.npairs + 1) + pr + 1) - e0) / G;   // exact tiles
+  const int ntiles = n_ex + (p.C + BLK - 1) / BLK;
 
   // Direct-to-LDS fetch of one K or V tile: the lane filling physical LDS slot (row, pc)
   // reads logical chunk pc ^ swz_key(row); each wave instruction fills 1 KB of consecutive
@@ -175,6 +195,47 @@ fwd_bf16_kernel(FwdArgs p) {
   constexpr int ROWS_I = THREADS / NCH;
   static_assert(ROWS_I % 16 == 0, "swizzle key must repeat across fetch passes");
   const int f_off0 = (tid / NCH) * (D * 2) + (((tid % NCH) ^ swz_key<D>(tid / NCH)) << 4);
+  // Exact tiles: tile row r holds key row (r % S) of the tile's key block r / S. A key
+  // block of S >= ROWS_I rows fills whole passes (the block's offset is the pass's scalar
+  // offset); smaller ones split a pass, and each lane picks its block's offset (js = the
+  // lane's block within the pass). S is a multiple of 16, so the swizzle key of a tile row
+  // is that of its key row.
+  constexpr int KBB = S * D * 2;   // bytes of one key block
+  const int js = (tid / NCH) / S;
+  auto fetch_exact = [&](__amdgpu_buffer_rsrc_t r, const int (&en)[G], bool partial,
+                         char* lds_tile) {
+    if (!partial) {
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        auto* dst = (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16);
+        if constexpr (S >= ROWS_I) {
+          const int j = (i * ROWS_I) / S;
+          const int soff = (en[j] & kEntIndex) * KBB + ((i * ROWS_I) % S) * (D * 2);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, f_off0, soff, 0, 0);
+        } else {
+          constexpr int R = ROWS_I / S;
+          const int kb = pick<R>(en, i * R, js) & kEntIndex;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, f_off0 + (kb - js) * KBB, 0, 0, 0);
+        }
+      }
+    } else {
+      // a key block past N: its missing rows re-read the block's last key (masked to -inf)
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        const int slot = i * THREADS + tid;
+        const int row = slot / NCH;
+        const int pc = slot - row * NCH;
+        const int kb = pick<G>(en, 0, row / S) & kEntIndex;
+        const int valid = min(S, p.N - kb * S);
+        const int off = (kb * S + min(row % S, valid - 1)) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds_tile + (i * THREADS + w * 64) * 16),
+            16, off, 0, 0, 0);
+      }
+    }
+  };
+  // Cluster tiles: C rows of the cache arrays taken BLK at a time; a short last tile
+  // re-reads its last row.
   auto fetch = [&](__amdgpu_buffer_rsrc_t r, int base, int valid, char* lds_tile) {
     if (valid == BLK) {
 #pragma unroll
@@ -195,9 +256,11 @@ fwd_bf16_kernel(FwdArgs p) {
       }
     }
   };
-  // Bias rows (log2 domain): thread tid < 2*BLK owns [tid / BLK][tid % BLK]: 0 / -inf past
-  // N for a ragged exact block, log2 n[b][c] or -inf for a cluster tile.
-  const int bq = b0 + tid / BLK;
+  // Bias rows (log2 domain): thread tid < 2*BLK owns [tid / BLK][tid % BLK]: for an exact
+  // tile 0 where the row's key block is kept by that query block and the key exists, else
+  // -inf; for a cluster tile log2 n[b][c], or -inf where n = 0.
+  const int bhalf = tid / BLK;
+  const int bq = b0 + bhalf;
   const int brow = tid % BLK;
   const int32_t* cnt_row = p.counts + ((size_t)h * p.nb + min(bq, p.nb - 1)) * p.C;
   auto load_count = [&](const TileDesc& d) -> int {
@@ -207,18 +270,36 @@ fwd_bf16_kernel(FwdArgs p) {
   // Stored divided by the log2-domain scale: the score accumulators start from it, so the
   // softmax of every tile kind is exp2(scale * (b / scale + q.k) - m).
   const float inv_c2 = 1.f / p.scale_log2e;
-  auto bias_of = [&](const TileDesc& d, int n) -> float {
-    if (d.kind == 0) return 0.f;
-    if (d.kind == 1) return brow < d.valid ? 0.f : kNegInf;
+  auto bias_of = [&](const TileDesc& d, const int (&en)[G], int n) -> float {
+    if (d.kind == 0) {
+      const int e = pick<G>(en, 0, brow / S);
+      const int key = (e & kEntIndex) * S + brow % S;
+      return (((e >> (kEntUse0 + bhalf)) & 1) && key < p.N) ? 0.f : kNegInf;
+    }
     return n > 0 ? fast_log2((float)n) * inv_c2 : kNegInf;
+  };
+  auto fetch_tile = [&](const TileDesc& d, const int (&en)[G], char* kl, char* vl) {
+    if (d.kind == 0) {
+      fetch_exact(rK, en, d.partial, kl);
+      fetch_exact(rV, en, d.partial, vl);
+    } else {
+      fetch(rM, d.off, d.valid, kl);
+      fetch(rB, d.off, d.valid, vl);
+    }
+  };
+  // list entries of exact tile t (wave-uniform)
+  auto load_entries = [&](int t, int (&en)[G]) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) en[j] = t < n_ex ? sload(p.pcol, e0 + G * t + j) : 0;
   };
 
   // prologue: tile 0 into stage 0
-  TileDesc cur = tile_desc<D, BLK>(0, n_list, n_list > 0 ? sload(p.pcol, e0) : 0, p.N, p.C);
-  fetch(cur.kind == 2 ? rM : rK, cur.off, cur.valid, k_s0);
-  fetch(cur.kind == 2 ? rB : rV, cur.off, cur.valid, v_s0);
-  if (tid < 2 * BLK) bias_s0[tid] = bias_of(cur, load_count(cur));
-  int ent_next = n_list > 1 ? sload(p.pcol, e0 + 1) : 0;
+  int en[G];   // entries of the tile being prefetched
+  load_entries(0, en);
+  TileDesc cur = tile_desc<D, BLK, G>(0, n_ex, en, p.C);
+  fetch_tile(cur, en, k_s0, v_s0);
+  if (tid < 2 * BLK) bias_s0[tid] = bias_of(cur, en, load_count(cur));
+  load_entries(1, en);
 
   // Q^T operand for this lane's query, all d k-steps.
   const int q = bw * BLK + wq * 32 + l32;
@@ -256,11 +337,10 @@ fwd_bf16_kernel(FwdArgs p) {
 
     // prefetch tile t+1 into the other stage (free since the barrier closing tile t-1)
     const bool has_next = t + 1 < ntiles;
-    const TileDesc nxt = tile_desc<D, BLK>(t + 1, n_list, ent_next, p.N, p.C);
+    const TileDesc nxt = tile_desc<D, BLK, G>(t + 1, n_ex, en, p.C);
     int cnt_next = 0;
     if (has_next) {
-      fetch(nxt.kind == 2 ? rM : rK, nxt.off, nxt.valid, nk);
-      fetch(nxt.kind == 2 ? rB : rV, nxt.off, nxt.valid, nv);
+      fetch_tile(nxt, en, nk, nv);
       cnt_next = load_count(nxt);
     }
 
@@ -283,8 +363,9 @@ fwd_bf16_kernel(FwdArgs p) {
       // (u, t2) covers keys 32mk + 16t2 + {0..15}; this lane's eight k-values are keys
       // 32mk + 16t2 + 8i' + 4hl + j (i' = 0,1; j = 0..3) = score accumulators 8t2 .. 8t2+7).
       bf16x8 pk[2][KC][2];
-      // Scores start from the tile's bias row (0 for a full exact block, -inf past N, and
-      // log2 of the outside count for a cluster tile, all divided by the scale).
+      // Scores start from the tile's bias row (0 for a kept key, -inf for a key past N or of
+      // a key block the query block does not keep, and log2 of the outside count for a
+      // cluster tile, all divided by the scale).
       auto qk = [&](int ch, f32x16 (&sc)[KC]) {
 #pragma unroll
         for (int u = 0; u < KC; ++u)
@@ -382,10 +463,10 @@ fwd_bf16_kernel(FwdArgs p) {
       pv(NCK - 1, pk[(NCK - 1) & 1]);
     }
 
-    if (has_next && tid < 2 * BLK) bias_nxt[tid] = bias_of(nxt, cnt_next);
-    // list entry of tile t+2, read here so no scalar load is in flight during the compute
+    if (has_next && tid < 2 * BLK) bias_nxt[tid] = bias_of(nxt, en, cnt_next);
+    // list entries of tile t+2, read here so no scalar load is in flight during the compute
     // (an outstanding scalar load forces every LDS wait to drain completely)
-    ent_next = t + 2 < n_list ? sload(p.pcol, e0 + t + 2) : 0;
+    load_entries(t + 2, en);
     // all waves are done with this stage, and this thread's prefetch has landed
     __syncthreads();
     cur = nxt;
@@ -416,8 +497,10 @@ fwd_bf16_kernel(FwdArgs p) {
 }
 
 // ----------------------------------------------------------------------------- fp32
-// Same structure with the fp32 32x32x2 MFMA (full fp32 products). K rows are padded by one
-// float and V rows by four so the column-wise operand reads do not pile onto one bank.
+// Same structure with the fp32 32x32x2 MFMA (full fp32 products), one query block per
+// workgroup. An exact tile gathers the next BLK/S key blocks of the block's list (S, the key
+// block size, is a power of two dividing BLK). K rows are padded by one float and V rows by
+// four so the column-wise operand reads do not pile onto one bank.
 template <int D, int BLK>
 __global__ void __launch_bounds__(BLK * 2)
 fwd_f32_kernel(FwdArgs p) {
@@ -454,8 +537,12 @@ fwd_f32_kernel(FwdArgs p) {
   const int32_t* cnt_row = p.counts + ((size_t)h * p.nb + b) * p.C;
   const int mh = p.mask_heads == 1 ? 0 : h;
   const int e0 = p.rowptr[mh * (p.nb + 1) + b];
-  const int n_exact = p.rowptr[mh * (p.nb + 1) + b + 1] - e0;
-  const int ntiles = n_exact + (p.C + BLK - 1) / BLK;
+  const int n_exact = p.rowptr[mh * (p.nb + 1) + b + 1] - e0;   // exact key blocks
+  const int S = p.kblock;
+  const int sh = __builtin_ctz(S);
+  const int G = BLK >> sh;
+  const int n_ex = (n_exact + G - 1) / G;                         // exact tiles
+  const int ntiles = n_ex + (p.C + BLK - 1) / BLK;
 
   const int q = b * BLK + w * 32 + l32;
   float qreg[KS];
@@ -467,32 +554,34 @@ fwd_f32_kernel(FwdArgs p) {
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
   float m_run = -1e30f, l_run = 0.f;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const float *ksrc, *vsrc;
-    int valid, kind;
-    if (t < n_exact) {
-      const int kb = p.col[e0 + t];
-      ksrc = Kh + (size_t)kb * BLK * D;
-      vsrc = Vh + (size_t)kb * BLK * D;
-      valid = min(BLK, p.N - kb * BLK);
-      kind = valid < BLK ? 1 : 0;
-    } else {
-      const int c0 = (t - n_exact) * BLK;
-      ksrc = Mh + (size_t)c0 * D;
-      vsrc = Bh + (size_t)c0 * D;
-      valid = min(BLK, p.C - c0);
-      kind = 2;
+  // Source row of tile row `row`: an exact tile's row r is key (r % S) of its (r / S)-th
+  // key block, or no key (-1) past the list's end or past N; a cluster tile's row r is
+  // cluster c0 + r, or none past C.
+  auto src_row = [&](int t, int row) -> int {
+    if (t < n_ex) {
+      const int e = t * G + (row >> sh);
+      const int key = e < n_exact ? (p.col[e0 + e] << sh) + (row & (S - 1)) : p.N;
+      return key < p.N ? key : -1;
     }
+    const int c = (t - n_ex) * BLK + row;
+    return c < p.C ? c : -1;
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    const bool exact = t < n_ex;
+    const float* ksrc = exact ? Kh : Mh;
+    const float* vsrc = exact ? Vh : Bh;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int idx = i * THREADS + tid;
       const int row = idx / NC4;
       const int c4 = idx - row * NC4;
+      const int sr = src_row(t, row);
       f32x4 kv = f32x4{}, vv = f32x4{};
-      if (row < valid) {
-        kv = *reinterpret_cast<const f32x4*>(ksrc + (size_t)row * D + 4 * c4);
-        vv = *reinterpret_cast<const f32x4*>(vsrc + (size_t)row * D + 4 * c4);
+      if (sr >= 0) {
+        kv = *reinterpret_cast<const f32x4*>(ksrc + (size_t)sr * D + 4 * c4);
+        vv = *reinterpret_cast<const f32x4*>(vsrc + (size_t)sr * D + 4 * c4);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -501,11 +590,10 @@ fwd_f32_kernel(FwdArgs p) {
       }
     }
     if (tid < BLK) {
-      float bv = 0.f;
-      if (kind == 1) bv = tid < valid ? 0.f : kNegInf;
-      if (kind == 2) {
-        const int c = (t - n_exact) * BLK + tid;
-        const int n = c < p.C ? cnt_row[c] : 0;
+      const int sr = src_row(t, tid);
+      float bv = sr >= 0 ? 0.f : kNegInf;
+      if (!exact) {
+        const int n = sr >= 0 ? cnt_row[sr] : 0;
         bv = n > 0 ? fast_log2((float)n) : kNegInf;
       }
       bias_lds[tid] = bv;
@@ -585,26 +673,41 @@ static size_t fwd_lds_bytes(bool bf16) {
               : (size_t)BLK * (D + 1) * 4 + (size_t)BLK * (D + 4) * 4 + BLK * 4;
 }
 
-template <int D, int BLK>
-static hipError_t launch_fwd_t(const FwdArgs& a, bool bf16, hipStream_t stream) {
-  const size_t lds = fwd_lds_bytes<D, BLK>(bf16);
-  if (bf16) {
-    const int grid = 8 * a.xmax;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK>), dim3(grid), dim3(BLK * 4), 0, stream, a);
-  } else {
-    const int total = a.H * a.nb;
-    const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, BLK>), dim3(grid), dim3(BLK * 2), lds, stream, a);
-  }
+template <int D, int BLK, int S>
+static hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK, S>), dim3(8 * a.xmax), dim3(BLK * 4), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, bool bf16,
+template <int D, int BLK>
+static hipError_t launch_fwd_t(const FwdArgs& a, int kblock, bool bf16, hipStream_t stream) {
+  if (bf16) {
+    switch (kblock) {
+      case 16: return launch_bf16<D, BLK, 16>(a, stream);
+      case 32: return launch_bf16<D, BLK, 32>(a, stream);
+      case 64: return launch_bf16<D, BLK, 64>(a, stream);
+      case 128:
+        if constexpr (BLK >= 128) return launch_bf16<D, BLK, 128>(a, stream);
+        break;
+      default: break;
+    }
+    return hipErrorInvalidValue;
+  }
+  if (kblock < 16 || kblock > BLK || (kblock & (kblock - 1)) != 0) return hipErrorInvalidValue;
+  const int total = a.H * a.nb;
+  const int grid = ((total + 7) / 8) * 8;
+  const size_t lds = fwd_lds_bytes<D, BLK>(false);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, BLK>), dim3(grid), dim3(BLK * 2), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs& a, int head_dim, int block, int kblock, bool bf16,
                           hipStream_t stream) {
-  if (head_dim == 64 && block == 64) return launch_fwd_t<64, 64>(a, bf16, stream);
-  if (head_dim == 64 && block == 128) return launch_fwd_t<64, 128>(a, bf16, stream);
-  if (head_dim == 128 && block == 64) return launch_fwd_t<128, 64>(a, bf16, stream);
-  if (head_dim == 128 && block == 128) return launch_fwd_t<128, 128>(a, bf16, stream);
+  if (head_dim == 64 && block == 64) return launch_fwd_t<64, 64>(a, kblock, bf16, stream);
+  if (head_dim == 64 && block == 128) return launch_fwd_t<64, 128>(a, kblock, bf16, stream);
+  if (head_dim == 128 && block == 64) return launch_fwd_t<128, 64>(a, kblock, bf16, stream);
+  if (head_dim == 128 && block == 128) return launch_fwd_t<128, 128>(a, kblock, bf16, stream);
   return hipErrorInvalidValue;
 }
 

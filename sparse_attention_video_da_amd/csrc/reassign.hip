@@ -16,7 +16,9 @@
 //   6. sums          fixed-size segments of the sorted order give fp32 partial sums per
 //                    cluster run, then one wave per cluster adds its partials in order,
 //                    divides and rounds to the cache dtype (deterministic throughout).
-//   7. counts        n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c], per pair.
+//   7. counts        n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c], per pair
+//                    (with key blocks smaller than the query blocks: size[c] minus the
+//                    exact keys of cluster c, read from the assignments).
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -647,6 +649,59 @@ counts_kernel(const uint8_t* __restrict__ hist, const int32_t* __restrict__ size
   }
 }
 
+// Counts when the exact key blocks (S keys) are smaller than the query blocks: per pair,
+// n[b][c] starts from size[c] in LDS and every key of the union list's key blocks takes one
+// off the rows of the query blocks that keep it, read straight from the assignments (4 bytes
+// a key, where histograms of S-key blocks would cost C bytes per block). Integer LDS
+// atomics, so the result does not depend on their order. 256/S list entries per pass, U
+// passes in flight.
+__global__ void __launch_bounds__(256)
+counts_keys_kernel(const int32_t* __restrict__ assign, const int32_t* __restrict__ sizes,
+                   const int32_t* __restrict__ prowptr, const int32_t* __restrict__ pcol,
+                   int32_t* __restrict__ counts, int N, int C, int nb, int npairs,
+                   int mask_heads, int S) {
+  extern __shared__ int32_t cnt_lds[];   // [2][C]
+  const int h = blockIdx.y, pr = blockIdx.x, tid = threadIdx.x;
+  const int b0 = 2 * pr;
+  const bool has1 = b0 + 1 < nb;
+  const int mh = mask_heads == 1 ? 0 : h;
+  const int e0 = prowptr[mh * (npairs + 1) + pr], e1 = prowptr[mh * (npairs + 1) + pr + 1];
+  const int32_t* sz = sizes + (size_t)h * C;
+  for (int c = tid; c < C; c += 256) {
+    const int v = sz[c];
+    cnt_lds[c] = v;
+    cnt_lds[C + c] = v;
+  }
+  __syncthreads();
+  const int32_t* ah = assign + (size_t)h * N;
+  const int per = 256 / S;
+  const int sub = tid / S, r = tid % S;
+  constexpr int U = 4;
+  for (int e = e0 + sub; e < e1; e += U * per) {
+    int ent[U], c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ent[u] = e + u * per < e1 ? pcol[e + u * per] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = (ent[u] & kEntIndex) * S + r;
+      const bool used = (ent[u] >> kEntUse0) & 3;
+      c[u] = (used && key < N) ? ah[key] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c[u] < 0) continue;
+      if ((ent[u] >> kEntUse0) & 1) atomicSub(&cnt_lds[c[u]], 1);
+      if ((ent[u] >> kEntUse1) & 1) atomicSub(&cnt_lds[C + c[u]], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* dst = counts + ((size_t)h * nb + b0) * C;
+  for (int c = tid; c < C; c += 256) {
+    dst[c] = cnt_lds[c];
+    if (has1) dst[C + c] = cnt_lds[C + c];
+  }
+}
+
 // ----------------------------------------------------------------------------- launch
 template <int D>
 static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_t s) {
@@ -686,8 +741,13 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
                          0, s, a.part, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.C, nseg);
     }
   }
-  hipLaunchKernelGGL(counts_kernel, dim3(a.npairs, a.H), dim3(256), 0, s, a.hist, a.sizes,
-                     a.prowptr, a.pcol, a.counts, a.C, a.nb, a.npairs, a.mask_heads);
+  if (a.kblock == a.block)
+    hipLaunchKernelGGL(counts_kernel, dim3(a.npairs, a.H), dim3(256), 0, s, a.hist, a.sizes,
+                       a.prowptr, a.pcol, a.counts, a.C, a.nb, a.npairs, a.mask_heads);
+  else
+    hipLaunchKernelGGL(counts_keys_kernel, dim3(a.npairs, a.H), dim3(256),
+                       2 * a.C * sizeof(int32_t), s, a.assign, a.sizes, a.prowptr, a.pcol,
+                       a.counts, a.N, a.C, a.nb, a.npairs, a.mask_heads, a.kblock);
   return hipGetLastError();
 }
 
@@ -698,9 +758,13 @@ hipError_t launch_reassign(const ReassignArgs& a, int head_dim, bool bf16, hipSt
 }
 
 hipError_t prepare_reassign_kernels() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&block_hist_kernel),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&block_hist_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(8192 * sizeof(int32_t)));
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&counts_keys_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)(8192 * sizeof(int32_t)));
+                             (int)(2 * 8192 * sizeof(int32_t)));
 }
 
 }  // namespace da

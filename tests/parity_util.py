@@ -78,14 +78,14 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def check_reassign_head(K64, V64, mu0_64, mask, block, dtype, gpu: Dict[str, np.ndarray],
-                        what: str) -> Dict[str, int]:
+                        what: str, kblock: Optional[int] = None) -> Dict[str, int]:
     """Compare one head's GPU reassign outputs with the oracle's (same inputs).
 
     Assignments: identical wherever the oracle's top-two gap is >= 1e-4 (relative);
     inside the band the GPU's choice must be within 1e-4 of the minimum. Sizes, counts
     and means are compared exactly/within tolerance on every cluster that no
     band-disagreeing key touches; touched clusters get the sum and bound checks."""
-    ref = O.reassign_step(K64, V64, mu0_64, mask, block, dtype)
+    ref = O.reassign_step(K64, V64, mu0_64, mask, block, dtype, kblock=kblock)
     a_gpu = gpu["assign"].astype(np.int64)
     a_ref = ref["assign"]
     diff = a_gpu != a_ref
@@ -129,7 +129,8 @@ def check_reassign_head(K64, V64, mu0_64, mask, block, dtype, gpu: Dict[str, np.
 
 def oracle_forward_heads(L64: Dict[str, np.ndarray], caches: Dict[int, Dict[str, np.ndarray]],
                          mask: np.ndarray, block: int, heads: Iterable[int],
-                         qblocks: Optional[Dict[int, List[int]]] = None):
+                         qblocks: Optional[Dict[int, List[int]]] = None,
+                         kblock: Optional[int] = None):
     """Oracle outputs for selected heads (and optionally selected query blocks)."""
     out = {}
     for h in heads:
@@ -137,7 +138,7 @@ def oracle_forward_heads(L64: Dict[str, np.ndarray], caches: Dict[int, Dict[str,
         mh = mask[0] if mask.shape[0] == 1 else mask[h]
         qb = None if qblocks is None else qblocks[h]
         out[h] = O.forward(L64["Q"][h], L64["K"][h], L64["V"][h], c["mu1"], c["vbar"],
-                           c["counts"], mh, block, qblocks=qb)
+                           c["counts"], mh, block, qblocks=qb, kblock=kblock)
     return out
 
 

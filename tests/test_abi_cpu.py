@@ -50,11 +50,20 @@ def _ok_mask(n=8):
     ("heads", 0, 1), ("seq_len", 0, 1), ("clusters", 0, 1), ("clusters", 1001, 1),
     ("mask_heads", 3, 1), ("scale", -1.0, 1), ("scale", float("nan"), 1),
     ("head_dim", 96, 2), ("block", 32, 2), ("dtype", 7, 2), ("clusters", 900, 0),
+    ("key_block", -1, 1), ("key_block", 8, 2), ("key_block", 48, 2), ("key_block", 256, 2),
+    ("key_block", 16, 0), ("key_block", 32, 0), ("key_block", 64, 0), ("key_block", 128, 0),
 ])
 def test_descriptor_validation(S, field, value, code):
     d = S.make_desc(heads=2, seq_len=1000, head_dim=128, block=128, clusters=16)
     setattr(d, field, value)
     assert S.da_validate_desc(d, _ok_mask()) == code
+
+
+def test_key_block_above_query_block_is_unsupported(S):
+    d = S.make_desc(2, 1000, 128, 64, 16, key_block=128)
+    assert S.da_validate_desc(d, _ok_mask()) == S.DA_ERR_UNSUPPORTED
+    d.key_block = 64
+    assert S.da_validate_desc(d, _ok_mask()) == S.DA_OK
 
 
 def test_validation_rejects_null_mask_and_desc(S):

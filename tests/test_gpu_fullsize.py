@@ -62,7 +62,8 @@ def _step(lib, plan, cfg, L, mu0_stored, heads, qblocks, what):
                "counts": out["counts"][h].cpu().numpy(),
                "centroids": from_dev(out["centroids"][h], dt),
                "mean_values": from_dev(out["mean_values"][h], dt)}
-        r = check_reassign_head(K64, V64, mu0, mask_h(h), B, dt, got, f"{what} head {h}")
+        r = check_reassign_head(K64, V64, mu0, mask_h(h), B, dt, got, f"{what} head {h}",
+                                kblock=cfg.kblock)
         moves += r["band_moves"]
         caches[h] = r["ref"]
     say(f"  reassign ok on {len(heads)} heads ({moves} in-band moves)")
@@ -81,19 +82,21 @@ def _step(lib, plan, cfg, L, mu0_stored, heads, qblocks, what):
     for h in heads:
         ref, _ = O.forward(O.to_f64(L["Q"][h], dt), O.to_f64(L["K"][h], dt),
                            O.to_f64(L["V"][h], dt), caches[h]["mu1"], caches[h]["vbar"],
-                           caches[h]["counts"], mask_h(h), B, qblocks=qblocks)
+                           caches[h]["counts"], mask_h(h), B, qblocks=qblocks,
+                           kblock=cfg.kblock)
         got_all.append(from_dev(o[h][torch.from_numpy(rows).cuda()], dt))
         want_all.append(ref[rows])
     check_forward(np.concatenate(got_all), np.concatenate(want_all), dt, f"{what} forward")
     return caches, out["centroids"]
 
 
-@pytest.mark.parametrize("name", ["wan14b_bf16", "hunyuan13b_bf16", "hunyuan13b_budget_bf16"])
+@pytest.mark.parametrize("name", ["wan14b_bf16", "hunyuan13b_bf16", "hunyuan13b_budget_bf16",
+                                  "hunyuan13b_sub32_bf16"])
 def test_full_layer(lib, name):
     cfg = get_config(name)
     L = make_layer(cfg, threads=16)
     plan = lib.Plan(cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, L["mask"],
-                    dtype=cfg.dtype)
+                    dtype=cfg.dtype, key_block=cfg.kblock)
     heads = _sample_heads(cfg, 3, 11)
     qblocks = _sample_qblocks(cfg, 8, 12)
     _step(lib, plan, cfg, L, L["cache_init"], heads, qblocks, name)

@@ -53,9 +53,10 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     """GPU reassign + forward vs the oracle on the given heads (default: all)."""
     torch = torch_mod()
     H, N, d, B, C, dtype = (cfgd[k] for k in ("H", "N", "d", "B", "C", "dtype"))
+    S = cfgd.get("S") or B
     heads = list(range(H)) if heads is None else heads
-    say(f"[case] {what}: H={H} N={N} d={d} B={B} C={C} {dtype} exact={int(mask.sum())}")
-    plan = lib.Plan(H, N, d, B, C, mask, dtype=dtype)
+    say(f"[case] {what}: H={H} N={N} d={d} B={B} S={S} C={C} {dtype} exact={int(mask.sum())}")
+    plan = lib.Plan(H, N, d, B, C, mask, dtype=dtype, key_block=S)
     dev = {x: to_dev(L[x], dtype) for x in ("Q", "K", "V")}
     mu0 = to_dev(mu0_stored, dtype)
     L64 = _layer64(L, dtype)
@@ -71,11 +72,13 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
         moves = 0
         for h in heads:
             r = check_reassign_head(L64["K"][h], L64["V"][h], mu0_64[h], mask_h(h), B, dtype,
-                                    {k: v[h] for k, v in got.items()}, f"{what} head {h}")
+                                    {k: v[h] for k, v in got.items()}, f"{what} head {h}",
+                                    kblock=S)
             moves += r["band_moves"]
         say(f"  reassign ok ({len(heads)} heads, {moves} in-band moves)")
     # forward, teacher-forced with the oracle's refreshed cache
-    caches = {h: O.reassign_step(L64["K"][h], L64["V"][h], mu0_64[h], mask_h(h), B, dtype)
+    caches = {h: O.reassign_step(L64["K"][h], L64["V"][h], mu0_64[h], mask_h(h), B, dtype,
+                                 kblock=S)
               for h in heads}
     mu1 = np.zeros((H, C, d), np.float32 if dtype == "f32" else np.uint16)
     vb = np.zeros_like(mu1)
@@ -92,7 +95,8 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     got_all, want_all, lg, lw = [], [], [], []
     for h in heads:
         ref_o, ref_lse = O.forward(L64["Q"][h], L64["K"][h], L64["V"][h], caches[h]["mu1"],
-                                   caches[h]["vbar"], caches[h]["counts"], mask_h(h), B)
+                                   caches[h]["vbar"], caches[h]["counts"], mask_h(h), B,
+                                   kblock=S)
         got_all.append(o[h])
         want_all.append(ref_o)
         lg.append(lse[h])
@@ -110,7 +114,7 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
 
 def _cfgd(cfg, H=None):
     return dict(H=H or cfg.heads, N=cfg.seq_len, d=cfg.head_dim, B=cfg.block, C=cfg.clusters,
-                dtype=cfg.dtype)
+                dtype=cfg.dtype, S=cfg.kblock)
 
 
 # ----------------------------------------------------------------- named small configs
@@ -179,6 +183,80 @@ def test_cluster_count_edges(lib, N, C):
     mask = (rng.random((1, nb, nb)) < 0.35).astype(np.uint8)
     _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype="bf16"),
               f"clusters C={C} N={N}")
+
+
+# ----------------------------------------------------------------- key blocks smaller than B
+@pytest.mark.parametrize("name", ["small_sub32_bf16", "small_sub16_d64_bf16", "tiny_sub_f32"])
+def test_key_block_configs(lib, name):
+    """Exact key blocks of 32 or 16 keys packed into 128- or 64-row tiles: 3D-local masks
+    at the finer granularity (d = 64 with 16-key blocks splits every fetch pass across
+    four key blocks; N = 2700 and 1020 leave a partial last key block)."""
+    cfg = get_config(name)
+    L = make_layer(cfg)
+    assert L["mask"].shape[1:] == (cfg.num_blocks, cfg.num_key_blocks)
+    _run_case(lib, L, L["cache_init"], L["mask"], _cfgd(cfg), name)
+
+
+@pytest.mark.parametrize("d,B,S,dtype,N", [
+    (128, 128, 32, "bf16", 1000), (128, 128, 64, "bf16", 850), (128, 128, 16, "bf16", 1000),
+    (64, 128, 32, "bf16", 850), (64, 128, 16, "bf16", 1000), (128, 64, 32, "bf16", 1000),
+    (128, 64, 16, "bf16", 990), (64, 64, 32, "bf16", 980), (64, 64, 16, "bf16", 1000),
+    (128, 128, 32, "f32", 1000), (64, 64, 16, "f32", 1000), (128, 128, 64, "f32", 850)])
+def test_key_block_ragged(lib, d, B, S, dtype, N):
+    """Random per-head key-block masks (25%) with the awkward rows: one query block keeps
+    nothing, one keeps every key block, one keeps only the partial last key block, one keeps
+    a single key block (a tile padded with unused copies), and the two query blocks of a
+    pair keep disjoint sets (tiles of one user only, and mixed tiles at the seam). C = 200
+    gives a ragged cluster tile."""
+    H, C = 2, 200
+    L, cache = _random_layer(500 + d + B + S, H, N, d, dtype, C)
+    nb, nkb = -(-N // B), -(-N // S)
+    rng = np.random.default_rng(S + B)
+    mask = (rng.random((H, nb, nkb)) < 0.25).astype(np.uint8)
+    mask[0, 1, :] = 0
+    mask[1, 2, :] = 1
+    mask[0, 3, :] = 0
+    mask[0, 3, nkb - 1] = 1
+    mask[1, 0, :] = 0
+    mask[1, 0, 5] = 1
+    mask[0, 4, :] = 0
+    mask[0, 5, :] = 0
+    mask[0, 4, : nkb // 2: 3] = 1
+    mask[0, 5, nkb // 2:: 3] = 1
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype=dtype, S=S),
+              f"key blocks d{d} B{B} S{S} {dtype} N{N}")
+
+
+def test_key_block_plan_lists(lib):
+    """A key-block plan reports its exact lists in key blocks of the plan's size."""
+    cfg = get_config("small_sub32_bf16")
+    mask = block_mask(cfg)
+    plan = lib.Plan(2, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, mask,
+                    key_block=cfg.kblock)
+    rowptr, col = plan.exact_lists(0)
+    for b in range(cfg.num_blocks):
+        assert col[rowptr[b]:rowptr[b + 1]].tolist() == np.nonzero(mask[0, b])[0].tolist()
+    assert plan.info()["exact_pairs"] == int(mask.sum())
+    plan.close()
+
+
+def test_all_key_blocks_exact_is_dense(lib):
+    """Every 32-key block exact (N = 700: a partial last key block): dense attention."""
+    torch = torch_mod()
+    H, N, d, B, S, C = 1, 700, 128, 128, 32, 8
+    L, cache = _random_layer(6, H, N, d, "bf16", C)
+    mask = np.ones((1, -(-N // B), -(-N // S)), np.uint8)
+    plan = lib.Plan(H, N, d, B, C, mask, key_block=S)
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], to_dev(cache, "bf16"))
+    assert int(out["counts"].abs().sum().item()) == 0
+    o = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"],
+                     out["counts"])
+    torch.cuda.synchronize()
+    L64 = _layer64(L, "bf16")
+    want = O.dense_attention(L64["Q"][0], L64["K"][0], L64["V"][0])
+    check_forward(from_dev(o, "bf16")[0], want, "bf16", "all key blocks exact vs dense")
+    plan.close()
 
 
 def test_all_blocks_exact_is_dense(lib):
