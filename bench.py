@@ -61,14 +61,15 @@ def forward_source_sha() -> str:
     return hashlib.sha256(open(FORWARD_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(per_launch_units: int):
+def load_traffic(workload: str):
     """HBM bytes per forward launch from the committed rocprofv3 counter summary, or None
-    when it is missing or was taken on a different forward kernel source."""
+    when it is missing, covers another workload or was taken on a different forward kernel
+    source."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("forward_source_sha") != forward_source_sha():
+    if t.get("forward_source_sha") != forward_source_sha() or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -96,7 +97,7 @@ def cpu_baseline(cfg, L, mask, budget_s: float):
     a = O.assign(K[:nk], mu0)[0]
     a_full = np.concatenate([a, np.resize(a, cfg.seq_len - nk)]) if nk < cfg.seq_len else a
     t0 = time.perf_counter()
-    st = O.refresh(K, V, a_full, mu0, mask[0], cfg.block, cfg.dtype)
+    st = O.refresh(K, V, a_full, mu0, mask[0], cfg.block, cfg.dtype, kblock=cfg.kblock)
     t_refresh = time.perf_counter() - t0
     # forward over a sample of query blocks, as many as fit the budget
     qb = list(np.random.default_rng(0).choice(nb, size=nb, replace=False))
@@ -106,7 +107,7 @@ def cpu_baseline(cfg, L, mask, budget_s: float):
         b = qb[done]
         t0 = time.perf_counter()
         O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], mask[0], cfg.block,
-                  qblocks=[b])
+                  qblocks=[b], kblock=cfg.kblock)
         t_fwd += time.perf_counter() - t0
         done += 1
     per_head_s = t_assign + t_refresh + t_fwd * nb / max(done, 1)
@@ -136,6 +137,7 @@ def main():
     if args.heads:
         cfg = cfg.with_heads(args.heads)
     H, N, d, B, C = cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters
+    Skb = cfg.kblock
     nb = cfg.num_blocks
     log(f"[bench] generating {cfg.name}: H={H} N={N} d={d} B={B} C={C} nb={nb}")
     t0 = time.time()
@@ -154,7 +156,7 @@ def main():
     Q, K, V = dev(L["Q"]), dev(L["K"]), dev(L["V"])
     cache = dev(L["cache_init"])
     del L["Q"]
-    plan = S.Plan(H, N, d, B, C, mask, dtype=cfg.dtype)
+    plan = S.Plan(H, N, d, B, C, mask, dtype=cfg.dtype, key_block=Skb)
     outs = [plan.reassign(K, V, cache), None]
     outs[1] = {k: torch.empty_like(v) for k, v in outs[0].items()}
     # warm the cache: 10 Lloyd steps on the device (untimed)
@@ -199,10 +201,11 @@ def main():
     log(f"[bench] {args.steps} steps: wall {wall_ms:.3f} ms/step, reassign {re_ms:.3f} ms, "
         f"forward {fw_ms:.3f} ms (median {fw_med:.3f})")
 
-    # exact (query block, key block) pairs over all heads: one shared mask or one per head
+    # exact (query block, key block) pairs over all heads: one shared mask or one per head;
+    # a pair is B queries against S keys: 2*B*S*d for the scores and as many for P V
     pairs_all = int(mask.sum()) * (H if mask.shape[0] == 1 else 1)
     pairs = pairs_all / H
-    exact_flop = 4.0 * B * B * d * pairs_all
+    exact_flop = 4.0 * B * Skb * d * pairs_all
     comp_flop = 4.0 * N * C * d * H
     dense_flop = 4.0 * N * N * d * H
     peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -212,7 +215,7 @@ def main():
                 + H * N * 4                   # assignments
                 + 2.0 * H * C * d * es        # refreshed centroids + means
                 + H * nb * C * 4.0)           # counts
-    traffic = load_traffic(1)
+    traffic = load_traffic(cfg.name)
     result = {
         "metric": "ms per attention layer + achieved MFMA bf16 TFLOPS fraction at 5% density",
         "value": round(wall_ms, 4),
@@ -228,16 +231,17 @@ def main():
         "data": "synthetic (seeded Gaussian-mixture Q/K, N(0,1) V, 3D-local position mask)",
         "config": {"workload": cfg.name, "heads": H, "seq_len": N, "latent": [cfg.frames,
                    cfg.height, cfg.width], "head_dim": d, "block": B, "clusters": C,
-                   "exact_blocks_per_row": cfg.blocks_per_row,
-                   "density": round(pairs / (nb * nb), 4), "mask_heads": int(mask.shape[0]),
+                   "key_block": Skb, "exact_blocks_per_row": cfg.blocks_per_row,
+                   "density": round(pairs / (nb * cfg.num_key_blocks), 4),
+                   "mask_heads": int(mask.shape[0]),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel": "fwd_bf16_kernel<128,128>" if
-                     cfg.dtype == "bf16" else "fwd_f32_kernel",
+                     "traffic": traffic, "kernel": f"fwd_bf16_kernel<{d},{B},{Skb}>" if
+                     cfg.dtype == "bf16" else f"fwd_f32_kernel<{d},{B}>",
                      "flops_per_launch": exact_flop,
-                     "flops_basis": "exact-block MFMA work, 4*B*B*d per (query block, exact "
-                                    "key block) pair"},
+                     "flops_basis": "exact-block MFMA work, 4*B*S*d per (query block, exact "
+                                    "key block of S keys) pair"},
         "breakdown": {
             "forward_ms": round(fw_ms, 4), "forward_ms_median": round(fw_med, 4),
             "forward_ms_p10_p90": [round(float(np.percentile(fw_all, 10)), 4),

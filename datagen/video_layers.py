@@ -8,10 +8,18 @@ uniformly, and K_t = centre + sigma * N(0, I), Q_t likewise with its own compone
 noise draws (K and Q share the head's centres); V ~ N(0, I). Values are produced in
 float32 and stored in the layer's dtype (bf16 by round-to-nearest-even, or float32).
 
+Optional positional locality (`locality` a > 0, off in every named workload): Q_t and K_t
+both gain a * phi(x_t), where x_t = (S*f, r, w) are the token's scaled 3D coordinates (S
+as in the local masks) and phi are d random Fourier features of x with frequencies
+N(0, I / l^2) and uniform phases, scaled so |phi| is about 1. Then phi(x).phi(y) is about
+exp(-|x - y|^2 / (2 l^2)), so every logit gains about scale * a^2 times a Gaussian of the
+query-key distance: attention that decays with 3D distance, the structure that makes
+position-fixed exact blocks worth keeping.
+
 Every random stream is seeded with numpy's SeedSequence over the tuple
 (config id, head, stream, step), so any single head can be regenerated on its own.
 Streams: 0 centres, 1 K components, 2 K noise, 3 Q components, 4 Q noise, 5 V,
-6 K drift, 7 V drift, 8 mask, 9 cache seed.
+6 K drift, 7 V drift, 8 mask, 9 cache seed, 10 positional features.
 
 The mask is a plan input: position-fixed exact key blocks per query block. Three kinds:
   * "random": the diagonal block plus (k - 1) distinct seeded other blocks per row;
@@ -19,7 +27,11 @@ The mask is a plan input: position-fixed exact key blocks per query block. Three
     centre and the key block's centre (S*df)^2 + dr^2 + dw^2 with S = Hs / 4, ties to the
     smaller block index; optionally every key block holding a token of frame 0 is kept
     first ("first-frame" blocks). Key blocks may be smaller than query blocks
-    (`key_block`); k then counts key blocks of that size;
+    (`key_block`); k then counts key blocks of that size. With `local_rule="reach"` the
+    distance of a key block is instead that from its centre to the nearest token of the
+    query block (the keys within reach of some query, not of the block's centre: for key
+    blocks shorter than the query block the centre rule keeps a ball that misses the keys
+    near the query block's ends);
   * "local_budget": the same nearest-block rule with a budget k[h][b] per head and query
     block (one mask per head). Budgets are k times a head factor and a block factor, each
     log-uniform in [1/2, 2] and seeded per head, rescaled so their mean over the layer is
@@ -39,6 +51,7 @@ import numpy as np
 
 STREAM_CENTRES, STREAM_KCOMP, STREAM_KNOISE, STREAM_QCOMP, STREAM_QNOISE = 0, 1, 2, 3, 4
 STREAM_V, STREAM_KDRIFT, STREAM_VDRIFT, STREAM_MASK, STREAM_CACHE = 5, 6, 7, 8, 9
+STREAM_POS = 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -64,6 +77,9 @@ class LayerConfig:
     drift_sigma: float = 0.05
     description: str = ""
     key_block: int = 0      # exact key block size (0: the query block size)
+    locality: float = 0.0   # amplitude a of the positional term of Q and K (0: none)
+    locality_len: float = 6.0   # its length scale l, in scaled 3D token coordinates
+    local_rule: str = "centre"  # key block distance for "local" masks: "centre" | "reach"
 
     @property
     def seq_len(self) -> int:
@@ -132,8 +148,10 @@ CONFIGS: Dict[str, LayerConfig] = {
         block=128, clusters=128, mask_kind="local", blocks_per_row=48, first_frame=False,
         mixture=64, sigma=0.3, dtype="bf16", steps=0, drift_k=False, drift_v=False,
         key_block=32,
+        local_rule="reach",
         description="4 heads, N=8192 (8x32x32), d=128, query blocks of 128, exact key blocks "
-                    "of 32: the 48 nearest per query block (18.75%, 3D-local)"),
+                    "of 32: the 48 nearest to some token of each query block (18.75%, "
+                    "3D-local)"),
     "small_sub16_d64_bf16": LayerConfig(
         "small_sub16_d64_bf16", 9, heads=3, frames=3, height=30, width=30, head_dim=64,
         block=128, clusters=64, mask_kind="local", blocks_per_row=48, first_frame=True,
@@ -153,15 +171,18 @@ CONFIGS: Dict[str, LayerConfig] = {
         block=128, clusters=512, mask_kind="local", blocks_per_row=184, first_frame=False,
         mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False, drift_v=False,
         key_block=32,
-        description="13B-class layer with exact key blocks of 32 keys: the 184 nearest per "
-                    "query block of 128, the same 5% of keys as 46 blocks of 128"),
+        local_rule="reach",
+        description="13B-class layer with exact key blocks of 32 keys: the 184 nearest to "
+                    "some token of each query block of 128, the same 5% of keys as 46 "
+                    "blocks of 128"),
     "hunyuan13b_sub64_bf16": LayerConfig(
         "hunyuan13b_sub64_bf16", 12, heads=24, frames=33, height=45, width=80, head_dim=128,
         block=128, clusters=512, mask_kind="local", blocks_per_row=92, first_frame=False,
         mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False, drift_v=False,
         key_block=64,
-        description="13B-class layer with exact key blocks of 64 keys: the 92 nearest per "
-                    "query block of 128 (5% of keys)"),
+        local_rule="reach",
+        description="13B-class layer with exact key blocks of 64 keys: the 92 nearest to "
+                    "some token of each query block of 128 (5% of keys)"),
     "extreme_cache_bf16": LayerConfig(
         "extreme_cache_bf16", 5, heads=40, frames=21, height=45, width=80, head_dim=128,
         block=128, clusters=512, mask_kind="local", blocks_per_row=6, first_frame=False,
@@ -220,8 +241,23 @@ def head_tensors(cfg: LayerConfig, head: int) -> Dict[str, np.ndarray]:
     qc = _rng(cfg, head, STREAM_QCOMP).integers(0, g, size=n)
     q = centres[qc] + sig * _rng(cfg, head, STREAM_QNOISE).standard_normal((n, d), dtype=np.float32)
     v = _rng(cfg, head, STREAM_V).standard_normal((n, d), dtype=np.float32)
+    if cfg.locality > 0:
+        pos = np.float32(cfg.locality) * _positional_features(cfg, head)
+        q += pos
+        k += pos
     return {"Q": _store(cfg, q), "K": _store(cfg, k), "V": _store(cfg, v),
             "k_component": kc.astype(np.int64)}
+
+
+def _positional_features(cfg: LayerConfig, head: int) -> np.ndarray:
+    """[N][d] float32 random Fourier features of the scaled 3D token coordinates."""
+    n, d, hw, w = cfg.seq_len, cfg.head_dim, cfg.height * cfg.width, cfg.width
+    t = np.arange(n, dtype=np.int64)
+    x = np.stack([cfg.local_scale * (t // hw), (t // w) % cfg.height, t % w], axis=1)
+    rng = _rng(cfg, head, STREAM_POS)
+    omega = rng.standard_normal((3, d)) / cfg.locality_len
+    phase = rng.uniform(0.0, 2.0 * math.pi, size=d)
+    return (math.sqrt(2.0 / d) * np.cos(x.astype(np.float64) @ omega + phase)).astype(np.float32)
 
 
 def drift_noise(cfg: LayerConfig, head: int, step: int, which: str) -> np.ndarray:
@@ -239,12 +275,18 @@ def apply_drift(cfg: LayerConfig, stored: np.ndarray, head: int, step: int,
 
 
 # ---------------------------------------------------------------- masks
+def _token_coords(cfg: LayerConfig) -> np.ndarray:
+    """(frame, row, column) of every token, float64 [N][3]."""
+    n, hw, w = cfg.seq_len, cfg.height * cfg.width, cfg.width
+    t = np.arange(n, dtype=np.int64)
+    return np.stack([t // hw, (t // w) % cfg.height, t % w], axis=1).astype(np.float64)
+
+
 def _block_centres(cfg: LayerConfig, size: Optional[int] = None) -> np.ndarray:
     """Mean (frame, row, column) of the tokens of each block of `size` tokens."""
-    n, hw, w = cfg.seq_len, cfg.height * cfg.width, cfg.width
+    n = cfg.seq_len
     b = cfg.block if size is None else size
-    t = np.arange(n, dtype=np.int64)
-    coords = np.stack([t // hw, (t // w) % cfg.height, t % w], axis=1).astype(np.float64)
+    coords = _token_coords(cfg)
     nb = -(-n // b)
     cen = np.zeros((nb, 3))
     for kb in range(nb):
@@ -305,19 +347,29 @@ def block_mask(cfg: LayerConfig) -> np.ndarray:
         return mask[None]
     if cfg.mask_kind != "local":
         raise ValueError(cfg.mask_kind)
+    if cfg.local_rule not in ("centre", "reach"):
+        raise ValueError(cfg.local_rule)
     nkb = cfg.num_key_blocks
     mask = np.zeros((nb, nkb), dtype=np.uint8)
     cen_q = _block_centres(cfg)
     cen = _block_centres(cfg, cfg.kblock)
     s = cfg.local_scale
+    scaled = np.array([s, 1.0, 1.0])
+    tok = _token_coords(cfg) * scaled
     forced = np.zeros(nkb, dtype=bool)
     if cfg.first_frame:
         hw = cfg.height * cfg.width
         forced[: (min(hw, cfg.seq_len) - 1) // cfg.kblock + 1] = True
     idx = np.arange(nkb)
     for b in range(nb):
-        diff = cen - cen_q[b]
-        dist2 = (s * diff[:, 0]) ** 2 + diff[:, 1] ** 2 + diff[:, 2] ** 2
+        if cfg.local_rule == "centre":
+            diff = cen - cen_q[b]
+            dist2 = (s * diff[:, 0]) ** 2 + diff[:, 1] ** 2 + diff[:, 2] ** 2
+        else:
+            q = tok[b * cfg.block:min(cfg.seq_len, (b + 1) * cfg.block)]
+            kc = cen * scaled
+            d2 = ((kc[None, :, :] - q[:, None, :]) ** 2).sum(axis=2)
+            dist2 = d2.min(axis=0)
         order = np.lexsort((idx, dist2))          # by distance, then by block index
         chosen = list(idx[forced][:k])
         for kb in order:

@@ -151,36 +151,51 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
     }
     p->rowptr[(size_t)mh * (nb + 1) + nb] = (int32_t)p->col.size();
   }
-  // Pair lists. With several key blocks per tile, the blocks both query blocks use come
-  // first and those of one query block after, so a tile mixes users at most at the two
-  // seams and a query block's waves skip the tiles that hold none of its keys.
+  // Pair lists. With several key blocks per tile, each tile holds key blocks of one set of
+  // users (both query blocks, only 2p, or only 2p+1), so a query block's waves skip the
+  // tiles that hold none of its keys and never compute a masked key block; each set is cut
+  // into tiles in ascending order (its last tile padded with copies of its last entry whose
+  // use bits are clear), and the tiles of the three sets are merged by first key block.
+  // The walk then stays ascending, as with one key block per tile: workgroups of
+  // neighbouring pairs, which run at the same time on one XCD, request the same key blocks
+  // close together in time and share them in L2.
   const int32_t npairs = (nb + 1) / 2;
   const bool partial_last = desc->seq_len % S != 0;
   p->npairs = npairs;
   p->prowptr.resize((size_t)desc->mask_heads * (npairs + 1));
-  std::vector<int32_t> only0, only1;
+  std::vector<int32_t> sets[3];
   for (int32_t mh = 0; mh < desc->mask_heads; ++mh) {
     const uint8_t* m = mask + (size_t)mh * nb * nkb;
     for (int32_t pr = 0; pr < npairs; ++pr) {
       p->prowptr[(size_t)mh * (npairs + 1) + pr] = (int32_t)p->pcol.size();
       const int32_t b0 = 2 * pr, b1 = 2 * pr + 1;
-      only0.clear();
-      only1.clear();
+      for (auto& v : sets) v.clear();
       for (int32_t kb = 0; kb < nkb; ++kb) {
         const int32_t f0 = m[(size_t)b0 * nkb + kb] ? 1 : 0;
         const int32_t f1 = (b1 < nb && m[(size_t)b1 * nkb + kb]) ? 1 : 0;
         if (!(f0 | f1)) continue;
         const int32_t ent = kb | (f0 << da::kEntUse0) | (f1 << da::kEntUse1) |
                             ((partial_last && kb == nkb - 1) ? 1 << da::kEntPartial : 0);
-        if (G == 1 || (f0 & f1)) p->pcol.push_back(ent);
-        else (f0 ? only0 : only1).push_back(ent);
+        if (G == 1) p->pcol.push_back(ent);
+        else sets[(f0 & f1) ? 0 : (f0 ? 1 : 2)].push_back(ent);
       }
-      p->pcol.insert(p->pcol.end(), only0.begin(), only0.end());
-      p->pcol.insert(p->pcol.end(), only1.begin(), only1.end());
-      const int32_t len = (int32_t)p->pcol.size() - p->prowptr[(size_t)mh * (npairs + 1) + pr];
-      if (G > 1 && len % G != 0) {
-        const int32_t pad = p->pcol.back() & ~((1 << da::kEntUse0) | (1 << da::kEntUse1));
-        for (int32_t i = len % G; i < G; ++i) p->pcol.push_back(pad);
+      if (G == 1) continue;
+      for (auto& v : sets)
+        if (v.size() % G != 0) {
+          const int32_t pad = v.back() & ~((1 << da::kEntUse0) | (1 << da::kEntUse1));
+          v.resize((v.size() / G + 1) * G, pad);
+        }
+      size_t at[3] = {0, 0, 0};
+      for (;;) {
+        int best = -1;
+        for (int i = 0; i < 3; ++i)
+          if (at[i] < sets[i].size() &&
+              (best < 0 || (sets[i][at[i]] & da::kEntIndex) < (sets[best][at[best]] & da::kEntIndex)))
+            best = i;
+        if (best < 0) break;
+        p->pcol.insert(p->pcol.end(), sets[best].begin() + at[best],
+                       sets[best].begin() + at[best] + G);
+        at[best] += G;
       }
     }
     p->prowptr[(size_t)mh * (npairs + 1) + npairs] = (int32_t)p->pcol.size();

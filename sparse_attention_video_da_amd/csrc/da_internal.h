@@ -7,9 +7,10 @@
 namespace da {
 
 // Pair-list entry: key block index | used by query block 2p | used by 2p+1 | the key block
-// runs past N. With B/S key blocks per tile (S < B) a pair's list holds the blocks both
-// query blocks use, then those only 2p uses, then those only 2p+1 uses (each ascending), and
-// is padded to a multiple of B/S with copies of its last entry whose use bits are clear.
+// runs past N. With G = B/S key blocks per tile (S < B) a pair's list is a sequence of
+// G-entry tiles, each holding key blocks of one set of users (both, only 2p, only 2p+1),
+// ascending by first key block; padding entries repeat a set's last entry with its use
+// bits clear.
 constexpr int32_t kEntIndex = 0x0fffffff;
 constexpr int kEntUse0 = 28, kEntUse1 = 29, kEntPartial = 30;
 

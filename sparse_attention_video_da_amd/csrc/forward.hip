@@ -54,9 +54,14 @@ __device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
   return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
 }
 
+// The list entries of one exact tile (the first G lanes are used). A vector value, not an
+// addressable array: an array passed between the helpers below gets placed in LDS by the
+// compiler, costing LDS traffic and full waits every tile.
+typedef int32_t ents_t __attribute__((ext_vector_type(8)));
+
 // en[first + j] for a per-lane j in [0, R): a chain of selects over scalar registers.
-template <int R, int G>
-__device__ __forceinline__ int pick(const int (&en)[G], int first, int j) {
+template <int R>
+__device__ __forceinline__ int pick(ents_t en, int first, int j) {
   int v = en[first];
 #pragma unroll
   for (int i = 1; i < R; ++i) v = j == i ? en[first + i] : v;
@@ -64,7 +69,7 @@ __device__ __forceinline__ int pick(const int (&en)[G], int first, int j) {
 }
 
 template <int D, int BLK, int G>
-__device__ __forceinline__ TileDesc tile_desc(int t, int n_ex, const int (&en)[G], int C) {
+__device__ __forceinline__ TileDesc tile_desc(int t, int n_ex, ents_t en, int C) {
   TileDesc d;
   if (t < n_ex) {
     int u = 0;
@@ -106,7 +111,7 @@ template <int D, int BLK, int S>
 __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdArgs p) {
   constexpr int G = BLK / S;       // exact key blocks per tile
-  static_assert(G * S == BLK && S >= 16, "key blocks must tile the query block");
+  static_assert(G * S == BLK && S >= 16 && G <= 8, "key blocks must tile the query block");
   constexpr int THREADS = BLK * 4;
   constexpr int WPB = BLK / 32;    // waves per query block
   constexpr int KT = BLK / 32;     // 32-key subtiles per key block
@@ -202,8 +207,7 @@ fwd_bf16_kernel(FwdArgs p) {
   // is that of its key row.
   constexpr int KBB = S * D * 2;   // bytes of one key block
   const int js = (tid / NCH) / S;
-  auto fetch_exact = [&](__amdgpu_buffer_rsrc_t r, const int (&en)[G], bool partial,
-                         char* lds_tile) {
+  auto fetch_exact = [&](__amdgpu_buffer_rsrc_t r, ents_t en, bool partial, char* lds_tile) {
     if (!partial) {
 #pragma unroll
       for (int i = 0; i < PER_T; ++i) {
@@ -258,27 +262,36 @@ fwd_bf16_kernel(FwdArgs p) {
   };
   // Bias rows (log2 domain): thread tid < 2*BLK owns [tid / BLK][tid % BLK]: for an exact
   // tile 0 where the row's key block is kept by that query block and the key exists, else
-  // -inf; for a cluster tile log2 n[b][c], or -inf where n = 0.
-  const int bhalf = tid / BLK;
+  // -inf; for a cluster tile log2 n[b][c], or -inf where n = 0. The owners are the first
+  // 2*BLK/64 waves, so the half is wave-uniform; the row is rebuilt from the lane id where
+  // it is used (from an opaque mask, so no register carries it across the tile loop).
+  const int bhalf = w / (BLK / 64);
   const int bq = b0 + bhalf;
-  const int brow = tid % BLK;
+  const bool bias_owner = w < 2 * BLK / 64;
+  auto brow_now = [&]() -> int {
+    uint32_t all = ~0u;
+    asm volatile("" : "+s"(all));
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u));
+    return ((w % (BLK / 64)) << 6) + ln;
+  };
   const int32_t* cnt_row = p.counts + ((size_t)h * p.nb + min(bq, p.nb - 1)) * p.C;
   auto load_count = [&](const TileDesc& d) -> int {
-    const int c = d.c0 + brow;
-    return (d.kind == 2 && tid < 2 * BLK && c < p.C && bq < p.nb) ? cnt_row[c] : 0;
+    const int c = d.c0 + brow_now();
+    return (d.kind == 2 && bias_owner && c < p.C && bq < p.nb) ? cnt_row[c] : 0;
   };
   // Stored divided by the log2-domain scale: the score accumulators start from it, so the
   // softmax of every tile kind is exp2(scale * (b / scale + q.k) - m).
   const float inv_c2 = 1.f / p.scale_log2e;
-  auto bias_of = [&](const TileDesc& d, const int (&en)[G], int n) -> float {
+  auto bias_of = [&](const TileDesc& d, ents_t en, int n) -> float {
     if (d.kind == 0) {
+      const int brow = brow_now();
       const int e = pick<G>(en, 0, brow / S);
       const int key = (e & kEntIndex) * S + brow % S;
       return (((e >> (kEntUse0 + bhalf)) & 1) && key < p.N) ? 0.f : kNegInf;
     }
     return n > 0 ? fast_log2((float)n) * inv_c2 : kNegInf;
   };
-  auto fetch_tile = [&](const TileDesc& d, const int (&en)[G], char* kl, char* vl) {
+  auto fetch_tile = [&](const TileDesc& d, ents_t en, char* kl, char* vl) {
     if (d.kind == 0) {
       fetch_exact(rK, en, d.partial, kl);
       fetch_exact(rV, en, d.partial, vl);
@@ -287,19 +300,31 @@ fwd_bf16_kernel(FwdArgs p) {
       fetch(rB, d.off, d.valid, vl);
     }
   };
-  // list entries of exact tile t (wave-uniform)
-  auto load_entries = [&](int t, int (&en)[G]) {
+  // list entries of exact tile t (wave-uniform). Every pair's list is a whole number of
+  // G-entry tiles, so a tile's entries start at a multiple of G: one scalar load of G words.
+  auto load_entries = [&](int t) -> ents_t {
+    ents_t en = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (t < n_ex) {
+      const int at = e0 + G * t;
+      if constexpr (G == 1) {
+        en[0] = sload(p.pcol, at);
+      } else {
+        typedef int32_t vG __attribute__((ext_vector_type(G)));
+        const vG v = *reinterpret_cast<const __attribute__((address_space(4))) vG*>(
+            (const __attribute__((address_space(4))) int32_t*)(p.pcol) + at);
 #pragma unroll
-    for (int j = 0; j < G; ++j) en[j] = t < n_ex ? sload(p.pcol, e0 + G * t + j) : 0;
+        for (int j = 0; j < G; ++j) en[j] = v[j];
+      }
+    }
+    return en;
   };
 
   // prologue: tile 0 into stage 0
-  int en[G];   // entries of the tile being prefetched
-  load_entries(0, en);
+  ents_t en = load_entries(0);   // entries of the tile being prefetched
   TileDesc cur = tile_desc<D, BLK, G>(0, n_ex, en, p.C);
   fetch_tile(cur, en, k_s0, v_s0);
-  if (tid < 2 * BLK) bias_s0[tid] = bias_of(cur, en, load_count(cur));
-  load_entries(1, en);
+  if (bias_owner) bias_s0[tid] = bias_of(cur, en, load_count(cur));
+  en = load_entries(1);
 
   // Q^T operand for this lane's query, all d k-steps.
   const int q = bw * BLK + wq * 32 + l32;
@@ -463,10 +488,10 @@ fwd_bf16_kernel(FwdArgs p) {
       pv(NCK - 1, pk[(NCK - 1) & 1]);
     }
 
-    if (has_next && tid < 2 * BLK) bias_nxt[tid] = bias_of(nxt, en, cnt_next);
+    if (has_next && bias_owner) bias_nxt[tid] = bias_of(nxt, en, cnt_next);
     // list entries of tile t+2, read here so no scalar load is in flight during the compute
     // (an outstanding scalar load forces every LDS wait to drain completely)
-    load_entries(t + 2, en);
+    en = load_entries(t + 2);
     // all waves are done with this stage, and this thread's prefetch has landed
     __syncthreads();
     cur = nxt;
