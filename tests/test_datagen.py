@@ -37,3 +37,76 @@ def test_budgets_are_seeded():
     a, b = budgets(cfg), budgets(cfg)
     assert (a == b).all() and a.shape == (cfg.heads, cfg.num_blocks)
     assert abs(a.mean() - cfg.blocks_per_row) < 0.5
+
+
+def test_key_block_masks_keep_k_key_blocks_around_the_query_block():
+    import dataclasses
+    for rule in ("centre", "reach"):
+        cfg = dataclasses.replace(get_config("small_sub32_bf16"), local_rule=rule)
+        m = block_mask(cfg)[0]
+        S, B = cfg.kblock, cfg.block
+        assert m.shape == (cfg.num_blocks, cfg.num_key_blocks)
+        assert (m.sum(axis=1) == cfg.blocks_per_row).all()
+        # the query block's own keys are the nearest: all B/S of its key blocks are kept
+        for b in range(cfg.num_blocks):
+            own = range(b * B // S, min(cfg.num_key_blocks, (b + 1) * B // S))
+            assert all(m[b, kb] for kb in own), (rule, b)
+
+
+def test_reach_rule_covers_the_query_block_ends():
+    """With 32-key blocks and query blocks of 1.6 raster rows (80 wide, as in the 13B-class
+    latent), the reach rule keeps key blocks next to both ends of the query block; the
+    centre rule keeps a ball around its middle that reaches less far along it."""
+    import dataclasses
+    from datagen.video_layers import _token_coords
+    base = dataclasses.replace(get_config("small_sub32_bf16"), frames=4, height=24, width=80)
+    cen, rea = (block_mask(dataclasses.replace(base, local_rule=r))[0] for r in ("centre", "reach"))
+    xyz = _token_coords(base) * np.array([base.local_scale, 1.0, 1.0])
+    S, B = base.kblock, base.block
+
+    def worst_reach(m):
+        # largest distance from a query token to the nearest kept key, over all queries
+        worst = 0.0
+        for b in range(0, base.num_blocks, 7):
+            keys = np.concatenate([np.arange(kb * S, (kb + 1) * S) for kb in np.nonzero(m[b])[0]])
+            q = xyz[b * B:(b + 1) * B]
+            d = ((q[:, None, :] - xyz[keys][None, :, :]) ** 2).sum(axis=2).min(axis=1)
+            worst = max(worst, float(d.max()))
+        return worst
+
+    def mean_kernel(m, ell=6.0):
+        # mean over queries of the kept Gaussian-kernel mass of 3D distance
+        tot = 0.0
+        for b in range(0, base.num_blocks, 7):
+            keys = np.concatenate([np.arange(kb * S, (kb + 1) * S) for kb in np.nonzero(m[b])[0]])
+            q = xyz[b * B:(b + 1) * B]
+            d2 = ((q[:, None, :] - xyz[keys][None, :, :]) ** 2).sum(axis=2)
+            tot += float(np.exp(-d2 / (2 * ell * ell)).sum())
+        return tot
+
+    assert worst_reach(rea) <= worst_reach(cen)
+    assert mean_kernel(rea) > mean_kernel(cen)
+
+
+def test_positional_locality_is_a_distance_kernel_and_off_by_default():
+    import dataclasses
+    from datagen.video_layers import _positional_features, head_tensors
+    base = get_config("small_bf16")
+    cfg = dataclasses.replace(base, locality=4.0, locality_len=3.0)
+    # phi(x).phi(y) ~ exp(-|x-y|^2 / (2 l^2)) along a row (unit steps), down a column and
+    # across frames. For one head the d frequencies are one Monte Carlo sample of that
+    # kernel (error about sqrt(1/(2d)) = 0.09 at d = 64, whatever the number of token
+    # pairs averaged); averaged over 8 heads with their own frequencies, 4 sigma is 0.13.
+    w = cfg.width
+    phis = [_positional_features(cfg, h).astype(np.float64) for h in range(8)]
+    assert np.allclose(np.mean([np.linalg.norm(p, axis=1).mean() for p in phis]), 1.0,
+                       atol=0.03)
+    for step, dist in ((1, 1.0), (3, 3.0), (w, 1.0), (cfg.height * w, cfg.local_scale)):
+        i = np.arange(0, cfg.seq_len - step, 97)
+        got = float(np.mean([(p[i] * p[i + step]).sum(axis=1).mean() for p in phis]))
+        assert abs(got - np.exp(-dist * dist / (2 * 9.0))) < 0.13, (step, got)
+    # locality 0 draws nothing and leaves the tensors bit-identical
+    a, b = head_tensors(base, 1), head_tensors(dataclasses.replace(base, locality=0.0), 1)
+    assert all((a[k] == b[k]).all() for k in ("Q", "K", "V"))
+    c = head_tensors(cfg, 1)
+    assert (c["V"] == a["V"]).all() and not (c["K"] == a["K"]).all()
