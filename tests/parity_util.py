@@ -78,14 +78,17 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def check_reassign_head(K64, V64, mu0_64, mask, block, dtype, gpu: Dict[str, np.ndarray],
-                        what: str, kblock: Optional[int] = None) -> Dict[str, int]:
+                        what: str, kblock: Optional[int] = None,
+                        ref: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, int]:
     """Compare one head's GPU reassign outputs with the oracle's (same inputs).
 
     Assignments: identical wherever the oracle's top-two gap is >= 1e-4 (relative);
     inside the band the GPU's choice must be within 1e-4 of the minimum. Sizes, counts
     and means are compared exactly/within tolerance on every cluster that no
-    band-disagreeing key touches; touched clusters get the sum and bound checks."""
-    ref = O.reassign_step(K64, V64, mu0_64, mask, block, dtype, kblock=kblock)
+    band-disagreeing key touches; touched clusters get the sum and bound checks. `ref` is the
+    oracle's step when it was computed elsewhere (see `OraclePool`)."""
+    if ref is None:
+        ref = O.reassign_step(K64, V64, mu0_64, mask, block, dtype, kblock=kblock)
     a_gpu = gpu["assign"].astype(np.int64)
     a_ref = ref["assign"]
     diff = a_gpu != a_ref
@@ -144,3 +147,77 @@ def oracle_forward_heads(L64: Dict[str, np.ndarray], caches: Dict[int, Dict[str,
 
 def rows_of(qblocks: List[int], block: int, n: int) -> np.ndarray:
     return np.concatenate([np.arange(b * block, min(n, (b + 1) * block)) for b in qblocks])
+
+
+# ----------------------------------------------------------------------------- oracle pool
+# Full-size layers have tens of heads: the oracle runs them in CPU worker processes (spawned,
+# one BLAS thread each; they never touch the GPU) while the test process drives the GPU.
+# A worker regenerates its head from the seeded generator (and its drift steps) instead of
+# receiving the tensors, so only caches, counts and masks cross the process boundary.
+_REF_KEYS = ("assign", "gap", "d1", "sizes", "counts", "mu1", "vbar", "mu1_exact", "vbar_exact")
+_HEAD_CACHE = {}
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _head(cfg, head: int, drift_steps: int):
+    """Stored Q, K, V of one head after `drift_steps` drift steps (as drift_layer makes them)."""
+    key = (cfg, head, drift_steps)
+    if key not in _HEAD_CACHE:
+        from datagen.video_layers import apply_drift, head_tensors
+        t = head_tensors(cfg, head)
+        for step in range(drift_steps):
+            for which, on in (("K", cfg.drift_k), ("V", cfg.drift_v)):
+                if on:
+                    t[which] = apply_drift(cfg, t[which], head, step, which)
+        _HEAD_CACHE.clear()
+        _HEAD_CACHE[key] = t
+    return _HEAD_CACHE[key]
+
+
+def _reassign_task(args):
+    cfg, head, drift_steps, mu0, mask = args
+    t = _head(cfg, head, drift_steps)
+    dt = cfg.dtype
+    ref = O.reassign_step(O.to_f64(t["K"], dt), O.to_f64(t["V"], dt), O.to_f64(mu0, dt), mask,
+                          cfg.block, dt, kblock=cfg.kblock)
+    return {k: ref[k] for k in _REF_KEYS}
+
+
+def _forward_task(args):
+    cfg, head, drift_steps, mu1, vbar, counts, mask, qblocks = args
+    t = _head(cfg, head, drift_steps)
+    dt = cfg.dtype
+    o, _ = O.forward(O.to_f64(t["Q"], dt), O.to_f64(t["K"], dt), O.to_f64(t["V"], dt), mu1, vbar,
+                     counts, mask, cfg.block, qblocks=qblocks, kblock=cfg.kblock)
+    return o[rows_of(qblocks, cfg.block, cfg.seq_len)]
+
+
+class OraclePool:
+    """Oracle steps of many heads of a generated layer, in parallel CPU processes."""
+
+    def __init__(self, workers: Optional[int] = None):
+        import multiprocessing as mp
+        import os
+        from concurrent.futures import ProcessPoolExecutor
+        n = workers or max(1, min(12, (os.cpu_count() or 2) - 2))
+        self.ex = ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"),
+                                      initializer=_one_blas_thread)
+
+    def reassign(self, tasks):
+        """tasks: (cfg, head, drift_steps, mu0 stored [C][d], mask [nb][nkb]) each."""
+        return list(self.ex.map(_reassign_task, tasks))
+
+    def forward(self, tasks):
+        """tasks: (cfg, head, drift_steps, mu1, vbar (float64), counts, mask, qblocks) each;
+        returns the oracle's output rows of each task's query blocks."""
+        return list(self.ex.map(_forward_task, tasks))
+
+    def close(self):
+        self.ex.shutdown()

@@ -1,19 +1,19 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
-Every head of the layer runs on the GPU; the oracle checks a seeded sample of heads (all
-keys: assignments, sizes, counts, centroids, mean values) and, for the forward, a sample
-of query blocks that always includes the first and the ragged last block. The forward of
-the sampled heads is teacher-forced with the oracle's refreshed cache (the other heads get
-the GPU's own refresh, which only fills the launch). Nothing the GPU produced is fed to
-the oracle.
+Every head of the layer runs on the GPU and every head is checked against the oracle for
+the reassign (assignments, sizes, counts, centroids, mean values, all keys). The forward of
+every head is then teacher-forced with the oracle's refreshed cache, and the oracle checks
+heads 0 and H-1 in full and 8 seeded query blocks (always the first and the ragged last) in
+every other head. The oracle runs in CPU worker processes that regenerate each head from the
+seeded generator. Nothing the GPU produced is fed to the oracle.
 """
 import numpy as np
 import pytest
 
 import oracle as O
-from datagen import drift_layer, get_config, make_layer
-from parity_util import (check_forward, check_reassign_head, from_dev, rows_of, say, store64,
-                         to_dev, torch_mod)
+from datagen import get_config, make_layer, drift_layer
+from parity_util import (OraclePool, check_forward, check_reassign_head, from_dev, rows_of,
+                         say, store64, to_dev, torch_mod)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -27,11 +27,11 @@ def lib():
     return S
 
 
-def _sample_heads(cfg, n, seed):
-    rng = np.random.default_rng(seed)
-    mid = [int(x) for x in rng.choice(np.arange(1, cfg.heads - 1), size=max(0, n - 2),
-                                      replace=False)]
-    return sorted({0, cfg.heads - 1, *mid})
+@pytest.fixture(scope="module")
+def pool():
+    p = OraclePool()
+    yield p
+    p.close()
 
 
 def _sample_qblocks(cfg, n, seed):
@@ -41,83 +41,79 @@ def _sample_qblocks(cfg, n, seed):
     return sorted({0, nb - 1, *mid})
 
 
-def _step(lib, plan, cfg, L, mu0_stored, heads, qblocks, what):
-    """GPU reassign + forward on all heads; oracle checks on `heads`. Returns the oracle
-    caches of the sampled heads (to teacher-force the next step) and the GPU's centroids."""
+def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what):
+    """GPU reassign + forward on all heads against the oracle (all heads for the reassign;
+    heads 0 and H-1 in full plus `qblocks` of every other head for the forward). Returns
+    the oracle's refreshed caches (stored), the next step's cache."""
     torch = torch_mod()
-    dt = cfg.dtype
-    B, C = cfg.block, cfg.clusters
+    dt, H, N, B, C = cfg.dtype, cfg.heads, cfg.seq_len, cfg.block, cfg.clusters
+    nb = cfg.num_blocks
     mask_h = (lambda h: L["mask"][0] if L["mask"].shape[0] == 1 else L["mask"][h])
-    say(f"[case] {what}: H={cfg.heads} N={cfg.seq_len} C={C} heads={heads}")
+    say(f"[case] {what}: H={H} N={N} C={C} S={cfg.kblock}")
     dev = {x: to_dev(L[x], dt) for x in ("Q", "K", "V")}
     out = plan.reassign(dev["K"], dev["V"], to_dev(mu0_stored, dt))
     torch.cuda.synchronize()
-    caches = {}
+    refs = pool.reassign([(cfg, h, drift_steps, mu0_stored[h], mask_h(h)) for h in range(H)])
+    got = {"assign": out["assign"].cpu().numpy(), "sizes": out["sizes"].cpu().numpy(),
+           "counts": out["counts"].cpu().numpy()}
     moves = 0
-    for h in heads:
-        K64 = O.to_f64(L["K"][h], dt)
-        V64 = O.to_f64(L["V"][h], dt)
-        mu0 = O.to_f64(mu0_stored[h], dt)
-        got = {"assign": out["assign"][h].cpu().numpy(), "sizes": out["sizes"][h].cpu().numpy(),
-               "counts": out["counts"][h].cpu().numpy(),
-               "centroids": from_dev(out["centroids"][h], dt),
-               "mean_values": from_dev(out["mean_values"][h], dt)}
-        r = check_reassign_head(K64, V64, mu0, mask_h(h), B, dt, got, f"{what} head {h}",
-                                kblock=cfg.kblock)
+    for h in range(H):
+        g = {k: v[h] for k, v in got.items()}
+        g["centroids"] = from_dev(out["centroids"][h], dt)
+        g["mean_values"] = from_dev(out["mean_values"][h], dt)
+        r = check_reassign_head(O.to_f64(L["K"][h], dt), None, O.to_f64(mu0_stored[h], dt),
+                                mask_h(h), B, dt, g, f"{what} head {h}", kblock=cfg.kblock,
+                                ref=refs[h])
         moves += r["band_moves"]
-        caches[h] = r["ref"]
-    say(f"  reassign ok on {len(heads)} heads ({moves} in-band moves)")
-    # forward: sampled heads get the oracle's cache, the rest the GPU's own refresh
-    mu1 = out["centroids"].clone()
-    vb = out["mean_values"].clone()
-    cnt = out["counts"].clone()
-    for h in heads:
-        mu1[h] = to_dev(store64(caches[h]["mu1"], dt), dt)
-        vb[h] = to_dev(store64(caches[h]["vbar"], dt), dt)
-        cnt[h] = torch.from_numpy(caches[h]["counts"].astype(np.int32)).cuda()
-    o = plan.forward(dev["Q"], dev["K"], dev["V"], mu1, vb, cnt)
+    say(f"  reassign ok on all {H} heads ({moves} in-band moves)")
+    # forward: every head teacher-forced with the oracle's refreshed cache
+    mu1 = np.stack([store64(refs[h]["mu1"], dt) for h in range(H)])
+    vb = np.stack([store64(refs[h]["vbar"], dt) for h in range(H)])
+    cnt = np.stack([refs[h]["counts"].astype(np.int32) for h in range(H)])
+    o = plan.forward(dev["Q"], dev["K"], dev["V"], to_dev(mu1, dt), to_dev(vb, dt),
+                     torch.from_numpy(cnt).cuda())
     torch.cuda.synchronize()
-    rows = rows_of(qblocks, B, cfg.seq_len)
-    got_all, want_all = [], []
-    for h in heads:
-        ref, _ = O.forward(O.to_f64(L["Q"][h], dt), O.to_f64(L["K"][h], dt),
-                           O.to_f64(L["V"][h], dt), caches[h]["mu1"], caches[h]["vbar"],
-                           caches[h]["counts"], mask_h(h), B, qblocks=qblocks,
-                           kblock=cfg.kblock)
-        got_all.append(from_dev(o[h][torch.from_numpy(rows).cuda()], dt))
-        want_all.append(ref[rows])
-    check_forward(np.concatenate(got_all), np.concatenate(want_all), dt, f"{what} forward")
-    return caches, out["centroids"]
+    full = {0, H - 1}
+    tasks = []
+    for h in range(H):
+        if h in full:
+            chunks = [list(range(s, min(nb, s + 128))) for s in range(0, nb, 128)]
+        else:
+            chunks = [qblocks]
+        for qb in chunks:
+            tasks.append((cfg, h, drift_steps, refs[h]["mu1"], refs[h]["vbar"], refs[h]["counts"],
+                          mask_h(h), qb))
+    want = pool.forward(tasks)
+    got_rows = []
+    for t in tasks:
+        rows = torch.from_numpy(rows_of(t[7], B, N)).cuda()
+        got_rows.append(from_dev(o[t[1]][rows], dt))
+    check_forward(np.concatenate(got_rows), np.concatenate(want), dt,
+                  f"{what} forward ({len(full)} full heads + {len(qblocks)} blocks of {H - 2})")
+    return mu1
 
 
 @pytest.mark.parametrize("name", ["wan14b_bf16", "hunyuan13b_bf16", "hunyuan13b_budget_bf16",
                                   "hunyuan13b_sub32_bf16"])
-def test_full_layer(lib, name):
+def test_full_layer(lib, pool, name):
     cfg = get_config(name)
     L = make_layer(cfg, threads=16)
     plan = lib.Plan(cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, L["mask"],
                     dtype=cfg.dtype, key_block=cfg.kblock)
-    heads = _sample_heads(cfg, 3, 11)
-    qblocks = _sample_qblocks(cfg, 8, 12)
-    _step(lib, plan, cfg, L, L["cache_init"], heads, qblocks, name)
+    _step(lib, plan, cfg, L, L["cache_init"], 0, pool, _sample_qblocks(cfg, 8, 12), name)
     plan.close()
 
 
-def test_extreme_cache_four_steps(lib):
-    """1% density, C = 512: four denoising steps, K and V drift each step; the cache of
-    the sampled heads is carried by the oracle (teacher forcing), the rest by the GPU."""
-    torch = torch_mod()
+def test_extreme_cache_four_steps(lib, pool):
+    """1% density, C = 512: four denoising steps, K and V drift each step; the oracle's
+    refreshed cache of every head is carried to the next step (teacher forcing)."""
     cfg = get_config("extreme_cache_bf16")
     L = make_layer(cfg, threads=16)
     plan = lib.Plan(cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, L["mask"],
                     dtype=cfg.dtype)
-    heads = _sample_heads(cfg, 2, 21)
-    qblocks = _sample_qblocks(cfg, 6, 22)
+    qblocks = _sample_qblocks(cfg, 8, 22)
     mu = L["cache_init"].copy()
     for step in range(cfg.steps):
         L = drift_layer(cfg, L, step, threads=16)
-        caches, gpu_mu = _step(lib, plan, cfg, L, mu, heads, qblocks, f"extreme step {step}")
-        mu = gpu_mu.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).copy()
-        for h in heads:
-            mu[h] = store64(caches[h]["mu1"], cfg.dtype)
+        mu = _step(lib, plan, cfg, L, mu, step + 1, pool, qblocks, f"extreme step {step}")
     plan.close()
