@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the reassign timing with the MALL flushed between reps")
+    ap.add_argument("--no-drift-chain", action="store_true",
+                    help="skip the per-step chain of a workload with denoising steps")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -112,11 +116,36 @@ def cpu_baseline(cfg, L, mask, budget_s: float):
         done += 1
     per_head_s = t_assign + t_refresh + t_fwd * nb / max(done, 1)
     ms_layer = per_head_s * cfg.heads * 1e3
-    return {"value": round(ms_layer, 1), "unit": "ms/layer", "cores": int(cores),
-            "kind": "oracle",
-            "sample": (f"head 0 of {cfg.heads}: assignment of {nk} of {cfg.seq_len} keys, "
-                       f"refresh+counts over all keys, forward of {done} of {nb} query blocks "
-                       f"(fp64 numpy); extrapolated linearly to all blocks and heads")}
+    out = {"value": round(ms_layer, 1), "unit": "ms/layer", "cores": int(cores),
+           "kind": "oracle",
+           "sample": (f"head 0 of {cfg.heads}: assignment of {nk} of {cfg.seq_len} keys, "
+                      f"refresh+counts over all keys, forward of {done} of {nb} query blocks "
+                      f"(fp64 numpy); extrapolated linearly to all blocks and heads")}
+    # the same with one BLAS thread, on a smaller sample (the refresh and counts are not
+    # threaded, so their time is reused)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            nk1 = min(cfg.seq_len, 4096)
+            t0 = time.perf_counter()
+            O.assign(K[:nk1], mu0)
+            t_assign1 = (time.perf_counter() - t0) * cfg.seq_len / nk1
+            done1, t_fwd1 = 0, 0.0
+            t_start = time.perf_counter()
+            while done1 < nb and (time.perf_counter() - t_start) < budget_s / 3:
+                t0 = time.perf_counter()
+                O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], mask[0], cfg.block,
+                          qblocks=[qb[done1]], kblock=cfg.kblock)
+                t_fwd1 += time.perf_counter() - t0
+                done1 += 1
+        per_head1 = t_assign1 + t_refresh + t_fwd1 * nb / max(done1, 1)
+        out["value_1_thread"] = round(per_head1 * cfg.heads * 1e3, 1)
+        out["sample_1_thread"] = (f"one BLAS thread: assignment of {nk1} keys, forward of "
+                                  f"{done1} query blocks, refresh time reused")
+    except Exception as e:  # reported, never fatal
+        out["value_1_thread"] = None
+        out["sample_1_thread"] = repr(e)
+    return out
 
 
 def main():
@@ -201,6 +230,55 @@ def main():
     log(f"[bench] {args.steps} steps: wall {wall_ms:.3f} ms/step, reassign {re_ms:.3f} ms, "
         f"forward {fw_ms:.3f} ms (median {fw_med:.3f})")
 
+    # reassign with the 256 MB MALL flushed before each rep (a 1 GiB device write between
+    # reps), for the HBM-bound reassign's cold-cache figure
+    flushed = []
+    if not args.no_flush:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        for i in range(5):
+            scratch.fill_(float(i))
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            plan.reassign(K, V, mu0, out=work)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            flushed.append(ev[0].elapsed_time(ev[1]))
+        del scratch
+        torch.cuda.empty_cache()
+
+    # denoising-step chain of a workload with drift: each step drifts K (and V) on the host,
+    # uploads them (untimed), runs the step 5 times untimed (the GPU idled during the host
+    # work and its clocks ramp up again), then times 5 more back-to-back reps of reassign
+    # from the carried cache and the forward (medians; the cache carried on is the step's
+    # refresh)
+    chain = []
+    if cfg.steps > 0 and not args.no_drift_chain:
+        from datagen import drift_layer
+        log(f"[bench] drift chain: {cfg.steps} steps")
+        cur_mu = mu0.clone()
+        Lh = L
+        for s_ in range(cfg.steps):
+            Lh = drift_layer(cfg, Lh, s_, threads=16)
+            Kd, Vd = dev(Lh["K"]), dev(Lh["V"])
+            torch.cuda.synchronize()
+            evs_c = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
+            for r in range(10):
+                evs_c[r][0].record(stream)
+                plan.reassign(Kd, Vd, cur_mu, out=work)
+                evs_c[r][1].record(stream)
+                plan.forward(Q, Kd, Vd, work["centroids"], work["mean_values"], work["counts"],
+                             out=O_out)
+                evs_c[r][2].record(stream)
+            torch.cuda.synchronize()
+            rs = [e[0].elapsed_time(e[1]) for e in evs_c[5:]]
+            fs = [e[1].elapsed_time(e[2]) for e in evs_c[5:]]
+            r_ms, f_ms = float(np.median(rs)), float(np.median(fs))
+            chain.append({"step": s_ + 1, "reassign_ms": round(r_ms, 4),
+                          "forward_ms": round(f_ms, 4), "layer_ms": round(r_ms + f_ms, 4)})
+            cur_mu = work["centroids"].clone()
+            del Kd, Vd
+        log(f"[bench] drift chain: " + ", ".join(f"{c['layer_ms']:.3f}" for c in chain) + " ms")
+
     # exact (query block, key block) pairs over all heads: one shared mask or one per head;
     # a pair is B queries against S keys: 2*B*S*d for the scores and as many for P V
     pairs_all = int(mask.sum()) * (H if mask.shape[0] == 1 else 1)
@@ -256,9 +334,15 @@ def main():
             "dense_equivalent_tflops": round(dense_flop / (fw_ms * 1e-3) / 1e12, 1),
             "reassign_algorithmic_gbs": round(re_bytes / (re_ms * 1e-3) / 1e9, 1),
             "reassign_hbm_frac": round(re_bytes / (re_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "reassign_ms_mall_flushed": round(float(np.median(flushed)), 4) if flushed else None,
+            "reassign_hbm_frac_mall_flushed": (round(re_bytes / (float(np.median(flushed)) * 1e-3)
+                                                     / 1e9 / HBM_PEAK_GBS, 4) if flushed else None),
         },
         "cpu_baseline": None,
     }
+    if chain:
+        result["drift_chain"] = {"steps": chain, "mean_layer_ms": round(
+            float(np.mean([c["layer_ms"] for c in chain])), 4)}
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle sample on the host ...")
         try:
