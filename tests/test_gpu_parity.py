@@ -259,6 +259,39 @@ def test_all_key_blocks_exact_is_dense(lib):
     plan.close()
 
 
+@pytest.mark.parametrize("N,C,d,B,S,dtype", [
+    (1, 1, 128, 128, None, "bf16"), (50, 3, 128, 128, None, "bf16"),
+    (50, 3, 128, 128, 32, "bf16"), (129, 5, 128, 128, 16, "bf16"), (129, 5, 64, 64, 16, "bf16"),
+    (1, 1, 64, 64, None, "f32"), (129, 5, 64, 64, None, "f32"), (70, 4, 64, 64, 16, "f32")])
+def test_tiny_layers(lib, N, C, d, B, S, dtype):
+    """Degenerate sizes: one token (one partial block, one cluster), fewer tokens than a
+    block, one token past a full block; head 0 keeps a random half of the key blocks (at
+    least the first), head 1 keeps none (pure compensation)."""
+    H = 2
+    L, cache = _random_layer(700 + N + C, H, N, d, dtype, C)
+    S_ = S or B
+    nb, nkb = -(-N // B), -(-N // S_)
+    rng = np.random.default_rng(N + 3 * C)
+    mask = (rng.random((H, nb, nkb)) < 0.5).astype(np.uint8)
+    mask[0, 0, 0] = 1
+    mask[1] = 0
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype=dtype, S=S),
+              f"tiny N={N} C={C} d{d} B{B} S{S_} {dtype}")
+
+
+@pytest.mark.parametrize("S", [None, 16])
+def test_max_clusters(lib, S):
+    """The largest cluster count the library accepts (C = 8192, 64 staging chunks in the
+    assignment, 64 KB of LDS counts per pair with key blocks), about one key per cluster."""
+    H, N, d, B, C = 1, 9000, 64, 64, 8192
+    L, cache = _random_layer(800 + (S or 0), H, N, d, "bf16", C, G=C // 4)
+    S_ = S or B
+    nb, nkb = -(-N // B), -(-N // S_)
+    mask = (np.random.default_rng(9).random((1, nb, nkb)) < 0.2).astype(np.uint8)
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype="bf16", S=S),
+              f"max clusters C={C} S{S_}")
+
+
 def test_all_blocks_exact_is_dense(lib):
     """Every block exact: the GPU output is dense attention (oracle's dense routine)."""
     torch = torch_mod()
