@@ -17,7 +17,11 @@ Pinning status: every public function is pinned by tests that do not retype it (
 forms, a hand-derived worked example, brute force, invariants and library special cases).
 Unpinned by the pages (a reading, not a derivation): whether the compensation centroid and
 mean value are global per cluster or restricted to keys outside the exact blocks; this
-oracle uses global per-cluster means (parity unpinned on that reading).
+oracle uses global per-cluster means (parity unpinned on that reading). The optional
+variance correction (`kvar` in `forward`, `key_variance`) is named by the ESTRA abstract
+without a formula: the second-order correction with an isotropic per-cluster variance is
+this oracle's reading; its arithmetic is pinned to closed forms and sampling, but that the
+pages mean exactly this is unpinned.
 """
 from .decoupattn_oracle import (  # noqa: F401
     TIE_BAND,
@@ -27,6 +31,7 @@ from .decoupattn_oracle import (  # noqa: F401
     assignment_allowed,
     refresh,
     qblock_counts_direct,
+    key_variance,
     forward,
     forward_substituted,
     dense_attention,

@@ -148,6 +148,24 @@ def qblock_counts_direct(a: np.ndarray, mask: np.ndarray, block: int, clusters: 
     return out
 
 
+def key_variance(K: np.ndarray, a: np.ndarray, mu1_exact: np.ndarray) -> np.ndarray:
+    """Isotropic spread of each cluster's keys around their mean:
+    kvar[c] = (1 / (N_c d)) sum_{j : a_j = c} ||k_j - mu_c||^2 (0 for an empty cluster).
+
+    The second moment a variance-based correction of the cluster representative's weight
+    needs (ESTRA abstract, the sentence on the variance-based correction; the pages give no
+    formula, see `forward`)."""
+    K = np.asarray(K, np.float64)
+    c, d = mu1_exact.shape
+    sq = np.zeros(c)
+    np.add.at(sq, a, ((K - mu1_exact[a]) ** 2).sum(axis=1))
+    n = np.bincount(a, minlength=c)
+    out = np.zeros(c)
+    has = n > 0
+    out[has] = sq[has] / (n[has] * d)
+    return out
+
+
 def refresh(K: np.ndarray, V: np.ndarray, a: np.ndarray, mu0: np.ndarray,
             mask: np.ndarray, block: int, dtype: str, kblock: Optional[int] = None
             ) -> Dict[str, np.ndarray]:
@@ -180,6 +198,7 @@ def refresh(K: np.ndarray, V: np.ndarray, a: np.ndarray, mu0: np.ndarray,
         "mu1": storage_round(mu1, dtype),
         "vbar": storage_round(vbar, dtype),
         "counts": qblock_counts_direct(a, mask, block, c, kblock),
+        "kvar": key_variance(K, a, mu1),
     }
 
 
@@ -204,8 +223,8 @@ def _exact_keys(mask_row: np.ndarray, block: int, n_tok: int) -> np.ndarray:
 
 def forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mu: np.ndarray, vbar: np.ndarray,
             counts: np.ndarray, mask: np.ndarray, block: int, scale: Optional[float] = None,
-            qblocks: Optional[Sequence[int]] = None, kblock: Optional[int] = None
-            ) -> Tuple[np.ndarray, np.ndarray]:
+            qblocks: Optional[Sequence[int]] = None, kblock: Optional[int] = None,
+            kvar: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Decoupled sparse attention output of one head (abstract: exact attention on a few
     position-fixed blocks, semantic clusters compensating every other key, one softmax).
 
@@ -215,6 +234,15 @@ def forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mu: np.ndarray, vbar: n
       o_i   = (sum_j e^{s_j - m} v_j + sum_c e^{t_c - m} vbar_c) / (sum of the same weights)
       lse_i = m + ln(sum of weights), m = the largest logit.
     The ln-count bias gives cluster c the weight of its n[b][c] stand-in keys.
+
+    With `kvar` (per-cluster key variance, `key_variance`), each cluster logit gains
+      + 0.5 * scale^2 * kvar[c] * ||q_i||^2,
+    the second-order correction of the representative's weight: for keys spread around mu_c
+    with covariance kvar[c] * I, the mean of exp(scale q.k) over them is
+    exp(scale q.mu_c + 0.5 scale^2 q^T Sigma q) exactly for Gaussian keys and to second
+    order otherwise (Jensen: the plain representative underweights a spread cluster). This
+    is the reading taken for the variance-based correction the ESTRA abstract names without
+    a formula.
 
     Returns (O [N][d], lse [N]); rows of query blocks not in `qblocks` are NaN."""
     Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
@@ -229,10 +257,11 @@ def forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mu: np.ndarray, vbar: n
         q = Q[rows]
         ex = _exact_keys(mask[b], block if kblock is None else kblock, n_tok)
         cs = np.nonzero(counts[b] > 0)[0]
-        logits = np.concatenate(
-            [scale * (q @ K[ex].T),
-             scale * (q @ mu[cs].T) + np.log(counts[b, cs].astype(np.float64))[None, :]],
-            axis=1)
+        comp = scale * (q @ mu[cs].T) + np.log(counts[b, cs].astype(np.float64))[None, :]
+        if kvar is not None:
+            qq = (q * q).sum(axis=1)
+            comp = comp + 0.5 * scale * scale * qq[:, None] * np.asarray(kvar, np.float64)[cs][None, :]
+        logits = np.concatenate([scale * (q @ K[ex].T), comp], axis=1)
         vals = np.concatenate([V[ex], vbar[cs]], axis=0)
         m = logits.max(axis=1, keepdims=True)
         w = np.exp(logits - m)

@@ -377,3 +377,74 @@ def test_key_block_count_invariants():
             if mask[b, j // S]:
                 inside[a[j]] += 1
         np.testing.assert_array_equal(cnt[b], sizes - inside)
+
+
+# ----------------------------------------------------------------- variance-corrected compensation
+def _one_cluster_lse(Q, K, kvar):
+    """lse of the forward with no exact block and every key in one cluster (centroid = mean)."""
+    n, d = K.shape
+    a = np.zeros(n, np.int64)
+    mu = K.mean(axis=0, keepdims=True)
+    counts = np.full((1, 1), n, np.int64)
+    mask = np.zeros((1, 1), np.uint8)
+    V = np.zeros_like(K)
+    _, lse = O.forward(Q, K, V, mu, np.zeros((1, d)), counts, mask, n, kvar=kvar)
+    return lse
+
+
+def test_variance_correction_is_second_order_exact():
+    """Keys mu +- delta e_i (2d keys): the sum of exp(s q.k) is exp(s q.mu) sum_i 2 cosh(s delta
+    q_i). The plain representative misses it at order delta^2; with kvar = delta^2 / d the
+    correction leaves an order-delta^4 residual (halving delta divides it by 16)."""
+    d = 6
+    rng = np.random.default_rng(90)
+    q = rng.standard_normal((1, d)) * 2.0
+    mu = rng.standard_normal(d)
+    s = O.default_scale(d)
+    errs_plain, errs_corr = [], []
+    for delta in (0.4, 0.2, 0.1):
+        K = np.concatenate([mu + delta * np.eye(d), mu - delta * np.eye(d)])
+        exact = s * q[0] @ mu + np.log(np.sum(2 * np.cosh(s * delta * q[0])))
+        kv = O.key_variance(K, np.zeros(2 * d, np.int64), K.mean(axis=0, keepdims=True))
+        assert kv[0] == pytest.approx(delta * delta / d, rel=1e-12)
+        errs_plain.append(abs(_one_cluster_lse(q, K, None)[0] - exact))
+        errs_corr.append(abs(_one_cluster_lse(q, K, kv)[0] - exact))
+    for e0, e1 in zip(errs_plain, errs_plain[1:]):
+        assert 3.5 < e0 / e1 < 4.5          # delta^2
+    for e0, e1 in zip(errs_corr, errs_corr[1:]):
+        assert 14.0 < e0 / e1 < 18.0        # delta^4
+    assert errs_corr[-1] < 1e-3 * errs_plain[-1]
+
+
+def test_variance_correction_matches_gaussian_keys():
+    """Isotropic Gaussian keys k = mu + sigma z: log of the mean of exp(s q.k) is
+    s q.mu + s^2 sigma^2 |q|^2 / 2; the corrected compensation reproduces it within the
+    sampling error while the plain one is off by that term."""
+    d, n, sigma = 8, 400_000, 0.5
+    rng = np.random.default_rng(91)
+    mu = rng.standard_normal(d)
+    K = mu + sigma * rng.standard_normal((n, d))
+    q = np.full((1, d), 1.5)
+    s = O.default_scale(d)
+    kv = O.key_variance(K, np.zeros(n, np.int64), K.mean(axis=0, keepdims=True))
+    assert kv[0] == pytest.approx(sigma * sigma, rel=1e-2)
+    logits = s * K @ q[0]
+    m = logits.max()
+    exact = m + np.log(np.exp(logits - m).sum())
+    term = 0.5 * s * s * sigma * sigma * float(q[0] @ q[0])
+    plain = _one_cluster_lse(q, K, None)[0]
+    corr = _one_cluster_lse(q, K, kv)[0]
+    assert abs(corr - exact) < 0.02 * term
+    assert abs((exact - plain) - term) < 0.02 * term
+
+
+def test_zero_variance_is_the_plain_forward():
+    Q, K, V, mask, B, st = _small_case(92)
+    o1, l1 = O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], mask, B)
+    o2, l2 = O.forward(Q, K, V, st["mu1"], st["vbar"], st["counts"], mask, B,
+                       kvar=np.zeros(st["mu1"].shape[0]))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    # a cluster holding one key has no spread
+    single = np.nonzero(st["sizes"] == 1)[0]
+    assert np.all(st["kvar"][single] == 0) and np.all(st["kvar"] >= 0)
