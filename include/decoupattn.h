@@ -142,6 +142,34 @@ DA_API da_status da_forward(da_plan plan, const void* Q, const void* K, const vo
                             const int32_t* qblock_counts, void* O, float* lse_out,
                             void* stream);
 
+/* Variance-corrected compensation (optional; the ESTRA page, "Extreme Sparsity Through
+ * Refined Attention", zhuanzhiai paper page, Abstract: a variance-based correction refines
+ * the attention weights of the cluster representatives; the page gives no formula, and the
+ * second-order correction below is this library's reading of it).
+ *
+ * da_reassign_var: da_reassign plus
+ *   key_variance_out  [H][C] float (4-byte aligned, device): kvar_c, the mean over the
+ *                     cluster's keys and the d dimensions of (k_j - mean_c)^2 (fp32, from the
+ *                     unrounded mean); 0 for an empty cluster. Must not overlap centroids_in.
+ * da_forward_var: da_forward where every cluster logit gains
+ *                 0.5 * scale^2 * key_variance[c] * ||q_i||^2
+ *   key_variance      [H][C] float (device), kvar >= 0 (for instance da_reassign_var's).
+ *                     With all zeros the result equals da_forward's.
+ * For keys spread around the centroid with covariance kvar * I the mean of exp(scale q.k)
+ * over them is exp(scale q.mean + 0.5 scale^2 kvar ||q||^2) (exact for Gaussian keys, to
+ * second order otherwise), so the corrected representative carries the cluster's weight
+ * instead of underestimating it (Jensen). Errors: as da_reassign / da_forward, and
+ * INVALID_ARGUMENT for a NULL or misaligned variance pointer. */
+DA_API da_status da_reassign_var(da_plan plan, const void* K, const void* V,
+                                 const void* centroids_in, void* centroids_out,
+                                 void* mean_values_out, int32_t* assign_out,
+                                 int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                                 float* key_variance_out, void* stream);
+DA_API da_status da_forward_var(da_plan plan, const void* Q, const void* K, const void* V,
+                                const void* centroids, const void* mean_values,
+                                const int32_t* qblock_counts, const float* key_variance,
+                                void* O, float* lse_out, void* stream);
+
 /* Plan introspection (host-side values; no device work).
  *   num_blocks       nb = ceil(N / block)
  *   exact_pairs      total number of (query block, exact key block) pairs over mask heads

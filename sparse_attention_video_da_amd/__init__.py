@@ -7,6 +7,6 @@ include/decoupattn.h); this package holds its sources (csrc/), the in-tree build
 from .binding import (  # noqa: F401
     DA_OK, DA_ERR_INVALID_ARGUMENT, DA_ERR_UNSUPPORTED, DA_ERR_OUT_OF_MEMORY, DA_ERR_DEVICE,
     DA_DTYPE_F32, DA_DTYPE_BF16, EXPORTED, LIB_PATH, DAError, Plan, da_desc, make_desc,
-    da_forward, da_plan_create, da_plan_destroy, da_reassign, da_status_str, da_validate_desc,
-    da_version,
+    da_forward, da_forward_var, da_plan_create, da_plan_destroy, da_reassign, da_reassign_var,
+    da_status_str, da_validate_desc, da_version,
 )

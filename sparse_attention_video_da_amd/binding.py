@@ -21,8 +21,9 @@ DA_OK, DA_ERR_INVALID_ARGUMENT, DA_ERR_UNSUPPORTED, DA_ERR_OUT_OF_MEMORY, DA_ERR
 DA_DTYPE_F32, DA_DTYPE_BF16 = 0, 1
 DTYPES = {"f32": DA_DTYPE_F32, "bf16": DA_DTYPE_BF16}
 
-EXPORTED = ("da_plan_create", "da_plan_destroy", "da_reassign", "da_forward", "da_plan_info",
-            "da_plan_exact_lists", "da_validate_desc", "da_status_str", "da_version")
+EXPORTED = ("da_plan_create", "da_plan_destroy", "da_reassign", "da_forward", "da_reassign_var",
+            "da_forward_var", "da_plan_info", "da_plan_exact_lists", "da_validate_desc",
+            "da_status_str", "da_version")
 
 
 class da_desc(ctypes.Structure):
@@ -61,6 +62,8 @@ def _load() -> ctypes.CDLL:
         "da_plan_destroy": ([vp], ctypes.c_int),
         "da_reassign": ([vp] + [vp] * 9, ctypes.c_int),
         "da_forward": ([vp] + [vp] * 9, ctypes.c_int),
+        "da_reassign_var": ([vp] + [vp] * 10, ctypes.c_int),
+        "da_forward_var": ([vp] + [vp] * 10, ctypes.c_int),
         "da_plan_info": ([vp, i32p, i64p, i64p], ctypes.c_int),
         "da_plan_exact_lists": ([vp, ctypes.c_int32, i32p, i32p], ctypes.c_int),
         "da_validate_desc": ([ctypes.POINTER(da_desc), u8p], ctypes.c_int),
@@ -127,6 +130,19 @@ def da_forward(handle, Q, K, V, centroids, mean_values, qblock_counts, O, lse_ou
                stream) -> int:
     return int(_lib.da_forward(handle, Q, K, V, centroids, mean_values, qblock_counts, O,
                                lse_out, stream))
+
+
+def da_reassign_var(handle, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
+                    cluster_sizes_out, qblock_counts_out, key_variance_out, stream) -> int:
+    return int(_lib.da_reassign_var(handle, K, V, centroids_in, centroids_out, mean_values_out,
+                                    assign_out, cluster_sizes_out, qblock_counts_out,
+                                    key_variance_out, stream))
+
+
+def da_forward_var(handle, Q, K, V, centroids, mean_values, qblock_counts, key_variance, O,
+                   lse_out, stream) -> int:
+    return int(_lib.da_forward_var(handle, Q, K, V, centroids, mean_values, qblock_counts,
+                                   key_variance, O, lse_out, stream))
 
 
 # ------------------------------------------------------------------------ torch wrapper
@@ -216,8 +232,10 @@ class Plan:
         s = torch.cuda.current_stream() if stream is None else stream
         return ctypes.c_void_p(s.cuda_stream)
 
-    def reassign(self, K, V, centroids_in, out: Optional[Dict] = None, stream=None):
-        """One Reassign Cache step. Returns dict(centroids, mean_values, assign, sizes, counts)."""
+    def reassign(self, K, V, centroids_in, out: Optional[Dict] = None, stream=None,
+                 variance: bool = False):
+        """One Reassign Cache step. Returns dict(centroids, mean_values, assign, sizes, counts),
+        plus `variance` ([H][C] float32 key variance, da_reassign_var) when variance=True."""
         torch = _torch()
         H, N, d, C, nb = self.heads, self.seq_len, self.head_dim, self.clusters, self.num_blocks
         self._check("K", K, (H, N, d))
@@ -232,22 +250,32 @@ class Plan:
                 "sizes": torch.empty((H, C), dtype=torch.int32, device=dev),
                 "counts": torch.empty((H, nb, C), dtype=torch.int32, device=dev),
             }
+            if variance:
+                out["variance"] = torch.empty((H, C), dtype=torch.float32, device=dev)
         else:
             self._check("centroids_out", out["centroids"], (H, C, d))
             self._check("mean_values_out", out["mean_values"], (H, C, d))
             self._check("assign_out", out["assign"], (H, N), torch.int32)
             self._check("sizes_out", out["sizes"], (H, C), torch.int32)
             self._check("counts_out", out["counts"], (H, nb, C), torch.int32)
-        st = da_reassign(self._h, _ptr(K), _ptr(V), _ptr(centroids_in), _ptr(out["centroids"]),
-                         _ptr(out["mean_values"]), _ptr(out["assign"]), _ptr(out["sizes"]),
-                         _ptr(out["counts"]), self._stream(stream))
+            if variance:
+                self._check("variance_out", out["variance"], (H, C), torch.float32)
+        args = (self._h, _ptr(K), _ptr(V), _ptr(centroids_in), _ptr(out["centroids"]),
+                _ptr(out["mean_values"]), _ptr(out["assign"]), _ptr(out["sizes"]),
+                _ptr(out["counts"]))
+        if variance:
+            st = da_reassign_var(*args, _ptr(out["variance"]), self._stream(stream))
+        else:
+            st = da_reassign(*args, self._stream(stream))
         if st != DA_OK:
-            raise DAError(st, "da_reassign")
+            raise DAError(st, "da_reassign_var" if variance else "da_reassign")
         return out
 
     def forward(self, Q, K, V, centroids, mean_values, counts, out=None, lse=False,
-                stream=None):
-        """Decoupled sparse attention. Returns O, or (O, lse) when lse=True."""
+                stream=None, variance=None):
+        """Decoupled sparse attention. Returns O, or (O, lse) when lse=True. With `variance`
+        ([H][C] float32 key variance) the cluster logits are variance-corrected
+        (da_forward_var)."""
         torch = _torch()
         H, N, d, C, nb = self.heads, self.seq_len, self.head_dim, self.clusters, self.num_blocks
         for name, t in (("Q", Q), ("K", K), ("V", V)):
@@ -265,8 +293,15 @@ class Plan:
         elif lse is not False and lse is not None:
             self._check("lse", lse, (H, N), torch.float32)
             lse_t = lse
-        st = da_forward(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(centroids), _ptr(mean_values),
-                        _ptr(counts), _ptr(out), _ptr(lse_t), self._stream(stream))
+        if variance is not None:
+            self._check("variance", variance, (H, C), torch.float32)
+            st = da_forward_var(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(centroids),
+                                _ptr(mean_values), _ptr(counts), _ptr(variance), _ptr(out),
+                                _ptr(lse_t), self._stream(stream))
+        else:
+            st = da_forward(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(centroids),
+                            _ptr(mean_values), _ptr(counts), _ptr(out), _ptr(lse_t),
+                            self._stream(stream))
         if st != DA_OK:
-            raise DAError(st, "da_forward")
+            raise DAError(st, "da_forward_var" if variance is not None else "da_forward")
         return (out, lse_t) if lse_t is not None else out

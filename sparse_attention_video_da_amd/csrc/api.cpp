@@ -44,6 +44,7 @@ struct da_plan_s {
   int32_t* d_perm = nullptr;
   int32_t* d_cop = nullptr;
   int32_t* d_part = nullptr;
+  int32_t* d_psq = nullptr;
   int64_t bytes = 0;
   int device = 0;
 };
@@ -89,11 +90,11 @@ da_status check_desc(const da_desc* d) {
 void destroy_device(da_plan_s* p) {
   int32_t* bufs[] = {p->d_rowptr, p->d_col,   p->d_prowptr, p->d_pcol,
                      p->d_hist,   p->d_off,   p->d_start,   p->d_perm, p->d_cop,
-                     p->d_part};
+                     p->d_part,   p->d_psq};
   for (int32_t* b : bufs)
     if (b) (void)hipFree(b);
   p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
-  p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = p->d_part = nullptr;
+  p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = p->d_part = p->d_psq = nullptr;
 }
 
 std::once_flag g_prep_once;
@@ -114,7 +115,7 @@ DA_API const char* da_status_str(da_status s) {
   return "unknown status";
 }
 
-DA_API int32_t da_version(void) { return 101; }
+DA_API int32_t da_version(void) { return 102; }
 
 DA_API da_status da_validate_desc(const da_desc* desc, const uint8_t* mask) {
   const da_status st = check_desc(desc);
@@ -248,7 +249,8 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
       {&p->d_pcol, n_pcol},       {&p->d_hist, (H * nb * C + 3) / 4}, {&p->d_off, H * nb * C},
       {&p->d_start, H * C},       {&p->d_perm, H * N},
       {&p->d_cop, (H * C * ((size_t)desc->head_dim + 8) * 2 + 3) / 4},
-      {&p->d_part, H * ((N + 255) / 256 + C) * 2 * (size_t)desc->head_dim}};
+      {&p->d_part, H * ((N + 255) / 256 + C) * 2 * (size_t)desc->head_dim},
+      {&p->d_psq, H * ((N + 255) / 256 + C)}};
   for (const Alloc& a : allocs) {
     if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -302,28 +304,35 @@ DA_API da_status da_plan_exact_lists(da_plan p, int32_t mh, int32_t* rowptr, int
   return DA_OK;
 }
 
-DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void* centroids_in,
-                             void* centroids_out, void* mean_values_out, int32_t* assign_out,
-                             int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+da_status reassign_impl(da_plan p, const void* K, const void* V, const void* centroids_in,
+                        void* centroids_out, void* mean_values_out, int32_t* assign_out,
+                        int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                        float* key_variance_out, bool want_variance, void* stream) {
   if (p == nullptr || K == nullptr || V == nullptr || centroids_in == nullptr ||
       centroids_out == nullptr || mean_values_out == nullptr || assign_out == nullptr ||
-      cluster_sizes_out == nullptr || qblock_counts_out == nullptr)
+      cluster_sizes_out == nullptr || qblock_counts_out == nullptr ||
+      (want_variance && key_variance_out == nullptr))
     return DA_ERR_INVALID_ARGUMENT;
   const da_desc& d = p->desc;
   const size_t es = elem_size(d);
   const size_t cache_bytes = (size_t)d.heads * d.clusters * d.head_dim * es;
   if (!aligned(K, 16) || !aligned(V, 16) || !aligned(centroids_in, 16) ||
       !aligned(centroids_out, 16) || !aligned(mean_values_out, 16) || !aligned(assign_out, 4) ||
-      !aligned(cluster_sizes_out, 4) || !aligned(qblock_counts_out, 4))
+      !aligned(cluster_sizes_out, 4) || !aligned(qblock_counts_out, 4) ||
+      (want_variance && !aligned(key_variance_out, 4)))
     return DA_ERR_INVALID_ARGUMENT;
   const size_t H = d.heads, N = d.seq_len, C = d.clusters;
   const void* outs[] = {centroids_out, mean_values_out, assign_out, cluster_sizes_out,
-                        qblock_counts_out};
+                        qblock_counts_out, key_variance_out};
   const size_t out_bytes[] = {cache_bytes, cache_bytes, H * N * 4, H * C * 4,
-                              H * (size_t)p->nb * C * 4};
-  for (int i = 0; i < 5; ++i)
-    if (overlap(centroids_in, cache_bytes, outs[i], out_bytes[i])) return DA_ERR_INVALID_ARGUMENT;
+                              H * (size_t)p->nb * C * 4, want_variance ? H * C * 4 : 0};
+  for (int i = 0; i < 6; ++i)
+    if (out_bytes[i] && overlap(centroids_in, cache_bytes, outs[i], out_bytes[i]))
+      return DA_ERR_INVALID_ARGUMENT;
   da::ReassignArgs a{};
   a.K = K;
   a.V = V;
@@ -344,6 +353,8 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
   a.perm = p->d_perm;
   a.cop = reinterpret_cast<uint16_t*>(p->d_cop);
   a.part = reinterpret_cast<float*>(p->d_part);
+  a.psq = reinterpret_cast<float*>(p->d_psq);
+  a.kvar = want_variance ? key_variance_out : nullptr;
   a.H = d.heads;
   a.N = d.seq_len;
   a.C = d.clusters;
@@ -356,16 +367,18 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
   return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;
 }
 
-DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void* V,
-                            const void* centroids, const void* mean_values,
-                            const int32_t* qblock_counts, void* O, float* lse_out,
-                            void* stream) {
+da_status forward_impl(da_plan p, const void* Q, const void* K, const void* V,
+                       const void* centroids, const void* mean_values,
+                       const int32_t* qblock_counts, const float* key_variance,
+                       bool want_variance, void* O, float* lse_out, void* stream) {
   if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || centroids == nullptr ||
-      mean_values == nullptr || qblock_counts == nullptr || O == nullptr)
+      mean_values == nullptr || qblock_counts == nullptr || O == nullptr ||
+      (want_variance && key_variance == nullptr))
     return DA_ERR_INVALID_ARGUMENT;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(centroids, 16) ||
       !aligned(mean_values, 16) || !aligned(O, 16) || !aligned(qblock_counts, 4) ||
-      (lse_out != nullptr && !aligned(lse_out, 4)))
+      (lse_out != nullptr && !aligned(lse_out, 4)) ||
+      (want_variance && !aligned(key_variance, 4)))
     return DA_ERR_INVALID_ARGUMENT;
   const da_desc& d = p->desc;
   da::FwdArgs a{};
@@ -391,10 +404,48 @@ DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void*
   a.mask_heads = d.mask_heads;
   a.kblock = p->kblock;
   a.scale_log2e = p->scale * 1.4426950408889634f;
+  a.kvar = want_variance ? key_variance : nullptr;
   const hipError_t e = da::launch_forward(a, d.head_dim, d.block, p->kblock,
                                           d.dtype == DA_DTYPE_BF16,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void* centroids_in,
+                             void* centroids_out, void* mean_values_out, int32_t* assign_out,
+                             int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                             void* stream) {
+  return reassign_impl(p, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
+                       cluster_sizes_out, qblock_counts_out, nullptr, false, stream);
+}
+
+DA_API da_status da_reassign_var(da_plan p, const void* K, const void* V,
+                                 const void* centroids_in, void* centroids_out,
+                                 void* mean_values_out, int32_t* assign_out,
+                                 int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                                 float* key_variance_out, void* stream) {
+  return reassign_impl(p, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
+                       cluster_sizes_out, qblock_counts_out, key_variance_out, true, stream);
+}
+
+DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void* V,
+                            const void* centroids, const void* mean_values,
+                            const int32_t* qblock_counts, void* O, float* lse_out,
+                            void* stream) {
+  return forward_impl(p, Q, K, V, centroids, mean_values, qblock_counts, nullptr, false, O,
+                      lse_out, stream);
+}
+
+DA_API da_status da_forward_var(da_plan p, const void* Q, const void* K, const void* V,
+                                const void* centroids, const void* mean_values,
+                                const int32_t* qblock_counts, const float* key_variance,
+                                void* O, float* lse_out, void* stream) {
+  return forward_impl(p, Q, K, V, centroids, mean_values, qblock_counts, key_variance, true, O,
+                      lse_out, stream);
 }
 
 }  // extern "C"

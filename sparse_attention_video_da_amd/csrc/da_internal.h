@@ -34,6 +34,7 @@ struct FwdArgs {
   int H, N, C, nb, mask_heads;
   int kblock;            // exact key block size S (divides the query block size)
   float scale_log2e;     // softmax scale * log2(e)
+  const float* kvar;     // [H][C] key variance for the variance-corrected cluster logits, or null
 };
 
 struct ReassignArgs {
@@ -56,6 +57,8 @@ struct ReassignArgs {
   int32_t* perm;   // workspace [H][N]
   uint16_t* cop;   // workspace: bf16 distance operands, [H][C][D] (-2 mu) then [H][C][8]
   float* part;     // workspace [H][ceil(N / 256) + C][2][D] partial sums of K and V
+  float* psq;      // workspace [H][ceil(N / 256) + C] partial sums of squared key norms
+  float* kvar;     // [H][C] key variance output, or null (not computed)
   int H, N, C, nb, block, mask_heads;
   int kblock;      // exact key block size S
 };

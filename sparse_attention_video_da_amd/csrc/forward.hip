@@ -107,7 +107,11 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
-template <int D, int BLK, int S>
+// VARC: variance-corrected cluster logits. Each cluster tile also carries a row
+// w_c = scale * kvar_c / 2 (in the score units), and the score accumulator of key row r and
+// this lane's query starts from bias_r + w_r * ||q||^2, so the cluster logit gains
+// scale^2 kvar_c ||q||^2 / 2 (exact-tile rows have w = 0).
+template <int D, int BLK, int S, bool VARC>
 __global__ void __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdArgs p) {
   constexpr int G = BLK / S;       // exact key blocks per tile
@@ -149,6 +153,8 @@ fwd_bf16_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(256))) char v_s1[TILE];
   __shared__ __attribute__((aligned(16))) float bias_s0[2 * BLK];   // [half][BLK]
   __shared__ __attribute__((aligned(16))) float bias_s1[2 * BLK];
+  __shared__ __attribute__((aligned(16))) float w_s0[VARC ? 2 * BLK : 4];   // VARC rows
+  __shared__ __attribute__((aligned(16))) float w_s1[VARC ? 2 * BLK : 4];
 
   // workgroup id L runs on XCD L % 8 and takes the next item of that XCD's range
   const int xcd = blockIdx.x & 7;
@@ -291,6 +297,12 @@ fwd_bf16_kernel(FwdArgs p) {
     }
     return n > 0 ? fast_log2((float)n) * inv_c2 : kNegInf;
   };
+  // VARC row of a tile (score units): scale * kvar / 2 for a cluster, 0 for an exact key
+  const float half_scale = 0.5f * p.scale_log2e * kLn2;
+  auto w_of = [&](const TileDesc& d) -> float {
+    const int c = d.c0 + brow_now();
+    return (d.kind == 2 && c < p.C) ? half_scale * p.kvar[(size_t)h * p.C + c] : 0.f;
+  };
   auto fetch_tile = [&](const TileDesc& d, ents_t en, char* kl, char* vl) {
     if (d.kind == 0) {
       fetch_exact(rK, en, d.partial, kl);
@@ -324,6 +336,9 @@ fwd_bf16_kernel(FwdArgs p) {
   TileDesc cur = tile_desc<D, BLK, G>(0, n_ex, en, p.C);
   fetch_tile(cur, en, k_s0, v_s0);
   if (bias_owner) bias_s0[tid] = bias_of(cur, en, load_count(cur));
+  if constexpr (VARC) {
+    if (bias_owner) w_s0[tid] = w_of(cur);
+  }
   en = load_entries(1);
 
   // Q^T operand for this lane's query, all d k-steps.
@@ -335,6 +350,19 @@ fwd_bf16_kernel(FwdArgs p) {
       qreg[s] = *reinterpret_cast<const bf16x8*>(Qh + ((size_t)q * D + 16 * s + 8 * hl) * 2);
     else
       qreg[s] = bf16x8{};
+  }
+  // ||q||^2 of this lane's query (VARC): this lane holds half of its dims, the lane 32 away
+  // the other half
+  float qn = 0.f;
+  if constexpr (VARC) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qreg[s][e];
+        qn = fmaf(x, x, qn);
+      }
+    qn += xor32(qn);
   }
 
   // Lane parts of the swizzled LDS read addresses. The swizzle key of a row depends only on
@@ -357,16 +385,19 @@ fwd_bf16_kernel(FwdArgs p) {
 
   // one tile: compute on (k_lds, v_lds, bias_cur) while tile t+1 streams into (nk, nv)
   auto tile = [&](int t, const char* k_lds, const char* v_lds, const float* bias_cur,
-                  char* nk, char* nv, float* bias_nxt) {
+                  const float* w_cur, char* nk, char* nv, float* bias_nxt, float* w_nxt) {
     const float* bias_lds = bias_cur + half * BLK;
+    const float* w_lds = w_cur + half * BLK;
 
     // prefetch tile t+1 into the other stage (free since the barrier closing tile t-1)
     const bool has_next = t + 1 < ntiles;
     const TileDesc nxt = tile_desc<D, BLK, G>(t + 1, n_ex, en, p.C);
     int cnt_next = 0;
+    float w_next = 0.f;
     if (has_next) {
       fetch_tile(nxt, en, nk, nv);
       cnt_next = load_count(nxt);
+      if constexpr (VARC) w_next = bias_owner ? w_of(nxt) : 0.f;
     }
 
     if (block_ok && ((cur.use >> half) & 1)) {
@@ -398,8 +429,15 @@ fwd_bf16_kernel(FwdArgs p) {
           for (int i = 0; i < 4; ++i) {
             const f32x4 bv = *reinterpret_cast<const f32x4*>(
                 bias_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
+            if constexpr (VARC) {
+              const f32x4 wv = *reinterpret_cast<const f32x4*>(
+                  w_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = bv[j];
+              for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = fmaf(wv[j], qn, bv[j]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = bv[j];
+            }
           }
 #pragma unroll
         for (int s = 0; s < DS; ++s)
@@ -489,6 +527,9 @@ fwd_bf16_kernel(FwdArgs p) {
     }
 
     if (has_next && bias_owner) bias_nxt[tid] = bias_of(nxt, en, cnt_next);
+    if constexpr (VARC) {
+      if (has_next && bias_owner) w_nxt[tid] = w_next;
+    }
     // list entries of tile t+2, read here so no scalar load is in flight during the compute
     // (an outstanding scalar load forces every LDS wait to drain completely)
     en = load_entries(t + 2);
@@ -497,8 +538,8 @@ fwd_bf16_kernel(FwdArgs p) {
     cur = nxt;
   };
   for (int t = 0; t < ntiles; t += 2) {
-    tile(t, k_s0, v_s0, bias_s0, k_s1, v_s1, bias_s1);
-    if (t + 1 < ntiles) tile(t + 1, k_s1, v_s1, bias_s1, k_s0, v_s0, bias_s0);
+    tile(t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+    if (t + 1 < ntiles) tile(t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
   }
 
   // Epilogue: normalise and store. Lane holds O[q][32dt + 8i + 4hl + j].
@@ -542,6 +583,7 @@ fwd_f32_kernel(FwdArgs p) {
   float* k_lds = reinterpret_cast<float*>(smem);
   float* v_lds = k_lds + BLK * KST;
   float* bias_lds = v_lds + BLK * VST;
+  float* w_lds = bias_lds + BLK;   // variance-correction row (log2 units), when p.kvar is set
 
   const int total = p.H * p.nb;
   const int logical = xcd_remap(blockIdx.x, total);
@@ -573,6 +615,13 @@ fwd_f32_kernel(FwdArgs p) {
   float qreg[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qreg[s] = q < p.N ? Qh[(size_t)q * D + 2 * s + hl] : 0.f;
+  // ||q||^2 (this lane holds the even or odd dims, the lane 32 away the others)
+  float qn = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qn = fmaf(qreg[s], qreg[s], qn);
+  qn += xor32(qn);
+  // log2 units: scale^2 * kvar / 2 * log2(e)
+  const float wscale = 0.5f * p.scale_log2e * p.scale_log2e * kLn2;
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -622,6 +671,9 @@ fwd_f32_kernel(FwdArgs p) {
         bv = n > 0 ? fast_log2((float)n) : kNegInf;
       }
       bias_lds[tid] = bv;
+      float wv = 0.f;
+      if (!exact && p.kvar != nullptr && sr >= 0) wv = wscale * p.kvar[(size_t)h * p.C + sr];
+      w_lds[tid] = wv;
     }
     __syncthreads();
 
@@ -640,7 +692,7 @@ fwd_f32_kernel(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * mk + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float x = sacc[mk][r] * p.scale_log2e + bias_lds[key];
+        const float x = sacc[mk][r] * p.scale_log2e + fmaf(w_lds[key], qn, bias_lds[key]);
         sacc[mk][r] = x;
         mloc = fmaxf(mloc, x);
       }
@@ -695,13 +747,17 @@ fwd_f32_kernel(FwdArgs p) {
 template <int D, int BLK>
 static size_t fwd_lds_bytes(bool bf16) {
   return bf16 ? (size_t)4 * BLK * D * 2 + 4 * BLK * 4
-              : (size_t)BLK * (D + 1) * 4 + (size_t)BLK * (D + 4) * 4 + BLK * 4;
+              : (size_t)BLK * (D + 1) * 4 + (size_t)BLK * (D + 4) * 4 + 2 * BLK * 4;
 }
 
 template <int D, int BLK, int S>
 static hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK, S>), dim3(8 * a.xmax), dim3(BLK * 4), 0, stream,
-                     a);
+  if (a.kvar != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK, S, true>), dim3(8 * a.xmax), dim3(BLK * 4), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BLK, S, false>), dim3(8 * a.xmax), dim3(BLK * 4), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -451,12 +451,21 @@ constexpr int kSeg = 256;
 #define SEG_U 16
 #endif
 
-template <int D, bool BF16>
+// Wave-wide sum (all 64 lanes receive it).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// With VAR, each partial also carries the sum of the squared norms of its keys (one float per
+// slot in psq), from which the finish derives the clusters' key variance.
+template <int D, bool BF16, bool VAR>
 __global__ void __launch_bounds__(256)
 segment_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
                    const int32_t* __restrict__ sizes, const int32_t* __restrict__ start,
-                   const int32_t* __restrict__ perm, float* __restrict__ part, int N, int C,
-                   int nseg) {
+                   const int32_t* __restrict__ perm, float* __restrict__ part,
+                   float* __restrict__ psq, int N, int C, int nseg) {
   constexpr int EPL = D / 64;
   constexpr int U = SEG_U;
   const int h = blockIdx.y;
@@ -476,6 +485,7 @@ segment_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
   int c = lo;
   int cend = st[c] + sz[c];
   float ks[EPL], vs[EPL];
+  float qs = 0.f;   // this lane's share of the squared key norms (VAR)
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ks[e] = vs[e] = 0.f;
   float* ph = part + (size_t)h * (nseg + C) * 2 * D;
@@ -486,6 +496,11 @@ segment_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
       o[e] = ks[e];
       o[D + e] = vs[e];
       ks[e] = vs[e] = 0.f;
+    }
+    if constexpr (VAR) {
+      const float t = wave_sum(qs);
+      if (lane == 0) psq[(size_t)h * (nseg + C) + sgi + c] = t;
+      qs = 0.f;
     }
   };
   auto load_row = [&](const void* base, int j, float* out) {
@@ -520,6 +535,7 @@ segment_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
         for (int e = 0; e < EPL; ++e) {
           ks[e] += kr[u][e];
           vs[e] += vr[u][e];
+          if constexpr (VAR) qs = fmaf(kr[u][e], kr[u][e], qs);
         }
         if (i + u + 1 == cend) {   // this cluster's run ends here
           flush();
@@ -533,10 +549,13 @@ segment_sum_kernel(const void* __restrict__ Kv, const void* __restrict__ Vv,
   if (c < C && st[c] < p1 && p1 < cend) flush();   // a run continuing into the next segment
 }
 
-template <int D, bool BF16>
+// With VAR, also the isotropic key variance of each cluster,
+// kvar = max(0, sum ||k||^2 / n - ||mean||^2) / D (fp32, from the unrounded mean; 0 if empty).
+template <int D, bool BF16, bool VAR>
 __global__ void __launch_bounds__(256)
-cluster_finish_kernel(const float* __restrict__ part, const void* __restrict__ mu_in,
-                      void* __restrict__ mu_out, void* __restrict__ vbar_out,
+cluster_finish_kernel(const float* __restrict__ part, const float* __restrict__ psq,
+                      const void* __restrict__ mu_in, void* __restrict__ mu_out,
+                      void* __restrict__ vbar_out, float* __restrict__ kvar_out,
                       const int32_t* __restrict__ sizes, const int32_t* __restrict__ start,
                       int C, int nseg) {
   constexpr int EPL = D / 64;
@@ -546,6 +565,7 @@ cluster_finish_kernel(const float* __restrict__ part, const void* __restrict__ m
   if (c >= C) return;
   const int cnt = sizes[(size_t)h * C + c];
   float ks[EPL], vs[EPL];
+  float sq = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ks[e] = vs[e] = 0.f;
   if (cnt > 0) {
@@ -559,10 +579,22 @@ cluster_finish_kernel(const float* __restrict__ part, const void* __restrict__ m
         ks[e] += q[e];
         vs[e] += q[D + e];
       }
+      if constexpr (VAR) sq += psq[(size_t)h * (nseg + C) + sg + c];
     }
   }
   const size_t o = ((size_t)h * C + c) * D + lane * EPL;
   const float fc = (float)cnt;
+  if constexpr (VAR) {
+    float m2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float m = cnt > 0 ? ks[e] / fc : 0.f;
+      m2 = fmaf(m, m, m2);
+    }
+    m2 = wave_sum(m2);
+    if (lane == 0)
+      kvar_out[(size_t)h * C + c] = cnt > 0 ? fmaxf(0.f, sq / fc - m2) / (float)D : 0.f;
+  }
   if constexpr (BF16) {
     uint16_t* mo = static_cast<uint16_t*>(mu_out) + o;
     uint16_t* vo = static_cast<uint16_t*>(vbar_out) + o;
@@ -703,6 +735,15 @@ counts_keys_kernel(const int32_t* __restrict__ assign, const int32_t* __restrict
 }
 
 // ----------------------------------------------------------------------------- launch
+template <int D, bool BF16, bool VAR>
+static void launch_sums(const ReassignArgs& a, int nseg, hipStream_t s) {
+  hipLaunchKernelGGL((segment_sum_kernel<D, BF16, VAR>), dim3((nseg + 3) / 4, a.H), dim3(256), 0,
+                     s, a.K, a.V, a.sizes, a.start, a.perm, a.part, a.psq, a.N, a.C, nseg);
+  hipLaunchKernelGGL((cluster_finish_kernel<D, BF16, VAR>), dim3((a.C + 3) / 4, a.H), dim3(256),
+                     0, s, a.part, a.psq, a.mu_in, a.mu_out, a.vbar_out, a.kvar, a.sizes, a.start,
+                     a.C, nseg);
+}
+
 template <int D>
 static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_t s) {
   if (bf16)
@@ -730,15 +771,11 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
   {
     const int nseg = (a.N + kSeg - 1) / kSeg;
     if (bf16) {
-      hipLaunchKernelGGL((segment_sum_kernel<D, true>), dim3((nseg + 3) / 4, a.H), dim3(256), 0,
-                         s, a.K, a.V, a.sizes, a.start, a.perm, a.part, a.N, a.C, nseg);
-      hipLaunchKernelGGL((cluster_finish_kernel<D, true>), dim3((a.C + 3) / 4, a.H), dim3(256),
-                         0, s, a.part, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.C, nseg);
+      if (a.kvar) launch_sums<D, true, true>(a, nseg, s);
+      else launch_sums<D, true, false>(a, nseg, s);
     } else {
-      hipLaunchKernelGGL((segment_sum_kernel<D, false>), dim3((nseg + 3) / 4, a.H), dim3(256), 0,
-                         s, a.K, a.V, a.sizes, a.start, a.perm, a.part, a.N, a.C, nseg);
-      hipLaunchKernelGGL((cluster_finish_kernel<D, false>), dim3((a.C + 3) / 4, a.H), dim3(256),
-                         0, s, a.part, a.mu_in, a.mu_out, a.vbar_out, a.sizes, a.start, a.C, nseg);
+      if (a.kvar) launch_sums<D, false, true>(a, nseg, s);
+      else launch_sums<D, false, false>(a, nseg, s);
     }
   }
   if (a.kblock == a.block)

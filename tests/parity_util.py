@@ -127,6 +127,14 @@ def check_reassign_head(K64, V64, mu0_64, mask, block, dtype, gpu: Dict[str, np.
             lim = 1e-5 * np.maximum(rms, 1e-3) + 1e-7
         err = np.abs(g - e)
         assert np.all(err <= lim), f"{what}: {name} off by {float((err / lim).max()):.2f} x tol"
+    if "variance" in gpu:
+        # fp32 sum of squared norms minus the squared fp32 mean: the error scales with the
+        # clusters' mean squared key element, sum ||k||^2 / (n d) = kvar + ||mean||^2 / d
+        ms = ref["kvar"] + (ref["mu1_exact"] ** 2).sum(axis=1) / ref["mu1_exact"].shape[1]
+        lim = 3e-5 * ms[keep] + 1e-9
+        err = np.abs(gpu["variance"].astype(np.float64)[keep] - ref["kvar"][keep])
+        assert np.all(err <= lim), f"{what}: variance off by {float((err / lim).max()):.2f} x tol"
+        assert np.all(gpu["variance"] >= 0), f"{what}: negative variance"
     return {"band_moves": int(diff.sum()), "keys": int(K64.shape[0]), "ref": ref}
 
 
@@ -154,7 +162,8 @@ def rows_of(qblocks: List[int], block: int, n: int) -> np.ndarray:
 # one BLAS thread each; they never touch the GPU) while the test process drives the GPU.
 # A worker regenerates its head from the seeded generator (and its drift steps) instead of
 # receiving the tensors, so only caches, counts and masks cross the process boundary.
-_REF_KEYS = ("assign", "gap", "d1", "sizes", "counts", "mu1", "vbar", "mu1_exact", "vbar_exact")
+_REF_KEYS = ("assign", "gap", "d1", "sizes", "counts", "mu1", "vbar", "mu1_exact", "vbar_exact",
+             "kvar")
 _HEAD_CACHE = {}
 
 
@@ -191,11 +200,12 @@ def _reassign_task(args):
 
 
 def _forward_task(args):
-    cfg, head, drift_steps, mu1, vbar, counts, mask, qblocks = args
+    cfg, head, drift_steps, mu1, vbar, counts, mask, qblocks = args[:8]
+    kvar = args[8] if len(args) > 8 else None
     t = _head(cfg, head, drift_steps)
     dt = cfg.dtype
     o, _ = O.forward(O.to_f64(t["Q"], dt), O.to_f64(t["K"], dt), O.to_f64(t["V"], dt), mu1, vbar,
-                     counts, mask, cfg.block, qblocks=qblocks, kblock=cfg.kblock)
+                     counts, mask, cfg.block, qblocks=qblocks, kblock=cfg.kblock, kvar=kvar)
     return o[rows_of(qblocks, cfg.block, cfg.seq_len)]
 
 
@@ -215,8 +225,8 @@ class OraclePool:
         return list(self.ex.map(_reassign_task, tasks))
 
     def forward(self, tasks):
-        """tasks: (cfg, head, drift_steps, mu1, vbar (float64), counts, mask, qblocks) each;
-        returns the oracle's output rows of each task's query blocks."""
+        """tasks: (cfg, head, drift_steps, mu1, vbar (float64), counts, mask, qblocks[, kvar])
+        each; returns the oracle's output rows of each task's query blocks."""
         return list(self.ex.map(_forward_task, tasks))
 
     def close(self):

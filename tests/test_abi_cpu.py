@@ -86,4 +86,6 @@ def test_plan_create_bad_desc_returns_before_device(S):
 def test_null_plan_is_rejected(S):
     assert S.da_forward(None, *([None] * 9)) == S.DA_ERR_INVALID_ARGUMENT
     assert S.da_reassign(None, *([None] * 9)) == S.DA_ERR_INVALID_ARGUMENT
+    assert S.da_forward_var(None, *([None] * 10)) == S.DA_ERR_INVALID_ARGUMENT
+    assert S.da_reassign_var(None, *([None] * 10)) == S.DA_ERR_INVALID_ARGUMENT
     assert S.da_plan_destroy(None) == S.DA_OK

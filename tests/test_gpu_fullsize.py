@@ -41,7 +41,7 @@ def _sample_qblocks(cfg, n, seed):
     return sorted({0, nb - 1, *mid})
 
 
-def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what):
+def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what, variance=False):
     """GPU reassign + forward on all heads against the oracle (all heads for the reassign;
     heads 0 and H-1 in full plus `qblocks` of every other head for the forward). Returns
     the oracle's refreshed caches (stored), the next step's cache."""
@@ -51,7 +51,7 @@ def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what):
     mask_h = (lambda h: L["mask"][0] if L["mask"].shape[0] == 1 else L["mask"][h])
     say(f"[case] {what}: H={H} N={N} C={C} S={cfg.kblock}")
     dev = {x: to_dev(L[x], dt) for x in ("Q", "K", "V")}
-    out = plan.reassign(dev["K"], dev["V"], to_dev(mu0_stored, dt))
+    out = plan.reassign(dev["K"], dev["V"], to_dev(mu0_stored, dt), variance=variance)
     torch.cuda.synchronize()
     refs = pool.reassign([(cfg, h, drift_steps, mu0_stored[h], mask_h(h)) for h in range(H)])
     got = {"assign": out["assign"].cpu().numpy(), "sizes": out["sizes"].cpu().numpy(),
@@ -61,6 +61,8 @@ def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what):
         g = {k: v[h] for k, v in got.items()}
         g["centroids"] = from_dev(out["centroids"][h], dt)
         g["mean_values"] = from_dev(out["mean_values"][h], dt)
+        if variance:
+            g["variance"] = out["variance"][h].cpu().numpy()
         r = check_reassign_head(O.to_f64(L["K"][h], dt), None, O.to_f64(mu0_stored[h], dt),
                                 mask_h(h), B, dt, g, f"{what} head {h}", kblock=cfg.kblock,
                                 ref=refs[h])
@@ -70,8 +72,10 @@ def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what):
     mu1 = np.stack([store64(refs[h]["mu1"], dt) for h in range(H)])
     vb = np.stack([store64(refs[h]["vbar"], dt) for h in range(H)])
     cnt = np.stack([refs[h]["counts"].astype(np.int32) for h in range(H)])
+    kv32 = np.stack([refs[h]["kvar"].astype(np.float32) for h in range(H)])
     o = plan.forward(dev["Q"], dev["K"], dev["V"], to_dev(mu1, dt), to_dev(vb, dt),
-                     torch.from_numpy(cnt).cuda())
+                     torch.from_numpy(cnt).cuda(),
+                     variance=torch.from_numpy(kv32).cuda() if variance else None)
     torch.cuda.synchronize()
     full = {0, H - 1}
     tasks = []
@@ -82,7 +86,7 @@ def _step(lib, plan, cfg, L, mu0_stored, drift_steps, pool, qblocks, what):
             chunks = [qblocks]
         for qb in chunks:
             tasks.append((cfg, h, drift_steps, refs[h]["mu1"], refs[h]["vbar"], refs[h]["counts"],
-                          mask_h(h), qb))
+                          mask_h(h), qb) + ((kv32[h].astype(np.float64),) if variance else ()))
     want = pool.forward(tasks)
     got_rows = []
     for t in tasks:
@@ -101,6 +105,17 @@ def test_full_layer(lib, pool, name):
     plan = lib.Plan(cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, L["mask"],
                     dtype=cfg.dtype, key_block=cfg.kblock)
     _step(lib, plan, cfg, L, L["cache_init"], 0, pool, _sample_qblocks(cfg, 8, 12), name)
+    plan.close()
+
+
+def test_full_layer_variance(lib, pool):
+    """The 13B-class layer through da_reassign_var / da_forward_var."""
+    cfg = get_config("hunyuan13b_bf16")
+    L = make_layer(cfg, threads=16)
+    plan = lib.Plan(cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, L["mask"],
+                    dtype=cfg.dtype)
+    _step(lib, plan, cfg, L, L["cache_init"], 0, pool, _sample_qblocks(cfg, 8, 13),
+          "hunyuan13b_bf16 var", variance=True)
     plan.close()
 
 

@@ -49,8 +49,10 @@ def _random_layer(seed, H, N, d, dtype, C, G=None, sigma=0.3):
     return out, cache
 
 
-def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=None):
-    """GPU reassign + forward vs the oracle on the given heads (default: all)."""
+def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=None,
+              variance=False):
+    """GPU reassign + forward vs the oracle on the given heads (default: all). With
+    variance=True the variance entry points run (key variances checked, forward corrected)."""
     torch = torch_mod()
     H, N, d, B, C, dtype = (cfgd[k] for k in ("H", "N", "d", "B", "C", "dtype"))
     S = cfgd.get("S") or B
@@ -63,12 +65,14 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     mu0_64 = np.stack([O.to_f64(mu0_stored[h], dtype) for h in range(H)])
     mask_h = (lambda h: mask[0] if mask.shape[0] == 1 else mask[h])
     if check_reassign:
-        out = plan.reassign(dev["K"], dev["V"], mu0)
+        out = plan.reassign(dev["K"], dev["V"], mu0, variance=variance)
         torch.cuda.synchronize()
         got = {"assign": out["assign"].cpu().numpy(), "sizes": out["sizes"].cpu().numpy(),
                "counts": out["counts"].cpu().numpy(),
                "centroids": from_dev(out["centroids"], dtype),
                "mean_values": from_dev(out["mean_values"], dtype)}
+        if variance:
+            got["variance"] = out["variance"].cpu().numpy()
         moves = 0
         for h in heads:
             r = check_reassign_head(L64["K"][h], L64["V"][h], mu0_64[h], mask_h(h), B, dtype,
@@ -83,12 +87,15 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     mu1 = np.zeros((H, C, d), np.float32 if dtype == "f32" else np.uint16)
     vb = np.zeros_like(mu1)
     cnt = np.zeros((H, plan.num_blocks, C), np.int32)
+    kv32 = np.zeros((H, C), np.float32)
     for h in heads:
         mu1[h] = store64(caches[h]["mu1"], dtype)
         vb[h] = store64(caches[h]["vbar"], dtype)
         cnt[h] = caches[h]["counts"]
+        kv32[h] = caches[h]["kvar"].astype(np.float32)
     o_dev, lse_dev = plan.forward(dev["Q"], dev["K"], dev["V"], to_dev(mu1, dtype),
-                                  to_dev(vb, dtype), torch.from_numpy(cnt).cuda(), lse=True)
+                                  to_dev(vb, dtype), torch.from_numpy(cnt).cuda(), lse=True,
+                                  variance=torch.from_numpy(kv32).cuda() if variance else None)
     torch.cuda.synchronize()
     o = from_dev(o_dev, dtype)
     lse = lse_dev.cpu().numpy().astype(np.float64)
@@ -96,7 +103,8 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     for h in heads:
         ref_o, ref_lse = O.forward(L64["Q"][h], L64["K"][h], L64["V"][h], caches[h]["mu1"],
                                    caches[h]["vbar"], caches[h]["counts"], mask_h(h), B,
-                                   kblock=S)
+                                   kblock=S,
+                                   kvar=kv32[h].astype(np.float64) if variance else None)
         got_all.append(o[h])
         want_all.append(ref_o)
         lg.append(lse[h])
@@ -290,6 +298,49 @@ def test_max_clusters(lib, S):
     mask = (np.random.default_rng(9).random((1, nb, nkb)) < 0.2).astype(np.uint8)
     _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype="bf16", S=S),
               f"max clusters C={C} S{S_}")
+
+
+# ----------------------------------------------------------------- variance-corrected compensation
+@pytest.mark.parametrize("name", ["small_bf16", "small_sub32_bf16", "tiny_f32", "tiny_sub_f32"])
+def test_variance_correction_configs(lib, name):
+    """da_reassign_var / da_forward_var on named layers (d = 64 and 128, key blocks of 128,
+    64, 32 and 16, bf16 and fp32): key variances against the oracle's, corrected forward
+    against the oracle's corrected forward."""
+    cfg = get_config(name)
+    L = make_layer(cfg)
+    _run_case(lib, L, L["cache_init"], L["mask"], _cfgd(cfg), name + " var", variance=True)
+
+
+@pytest.mark.parametrize("d,B,S,dtype,N", [(128, 128, 128, "bf16", 1000), (64, 128, 32, "bf16", 850),
+                                           (128, 64, 64, "f32", 1000)])
+def test_variance_correction_ragged(lib, d, B, S, dtype, N):
+    """Ragged shapes with the variance entry points: random masks, C = 200."""
+    H, C = 2, 200
+    L, cache = _random_layer(900 + d + B + S, H, N, d, dtype, C, sigma=0.5)
+    nb, nkb = -(-N // B), -(-N // S)
+    mask = (np.random.default_rng(S + 7).random((H, nb, nkb)) < 0.3).astype(np.uint8)
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype=dtype, S=S),
+              f"variance d{d} B{B} S{S} {dtype} N{N}", variance=True)
+
+
+def test_zero_variance_equals_plain_forward(lib):
+    """da_forward_var with all-zero variances reproduces da_forward bit for bit."""
+    torch = torch_mod()
+    H, N, d, B, C = 2, 900, 128, 128, 40
+    L, cache = _random_layer(11, H, N, d, "bf16", C)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(12).random((1, nb, nb)) < 0.4).astype(np.uint8)
+    plan = lib.Plan(H, N, d, B, C, mask)
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], to_dev(cache, "bf16"), variance=True)
+    o1 = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"],
+                      out["counts"])
+    o2 = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"],
+                      out["counts"], variance=torch.zeros((H, C), dtype=torch.float32,
+                                                          device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    plan.close()
 
 
 def test_all_blocks_exact_is_dense(lib):
