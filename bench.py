@@ -55,6 +55,8 @@ def parse():
                     help="skip the reassign timing with the MALL flushed between reps")
     ap.add_argument("--no-drift-chain", action="store_true",
                     help="skip the per-step chain of a workload with denoising steps")
+    ap.add_argument("--variance", action="store_true",
+                    help="time the variance-corrected step (da_reassign_var + da_forward_var)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -186,13 +188,14 @@ def main():
     cache = dev(L["cache_init"])
     del L["Q"]
     plan = S.Plan(H, N, d, B, C, mask, dtype=cfg.dtype, key_block=Skb)
-    outs = [plan.reassign(K, V, cache), None]
+    var = bool(args.variance)
+    outs = [plan.reassign(K, V, cache, variance=var), None]
     outs[1] = {k: torch.empty_like(v) for k, v in outs[0].items()}
     # warm the cache: 10 Lloyd steps on the device (untimed)
     cur = cache
     for i in range(10):
         o = outs[i % 2]
-        plan.reassign(K, V, cur, out=o)
+        plan.reassign(K, V, cur, out=o, variance=var)
         cur = o["centroids"]
     mu0 = cur.clone()
     work = {k: torch.empty_like(v) for k, v in outs[0].items()}
@@ -205,10 +208,11 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        plan.reassign(K, V, mu0, out=work)
+        plan.reassign(K, V, mu0, out=work, variance=var)
         if ev is not None:
             ev[1].record(stream)
-        plan.forward(Q, K, V, work["centroids"], work["mean_values"], work["counts"], out=O_out)
+        plan.forward(Q, K, V, work["centroids"], work["mean_values"], work["counts"], out=O_out,
+                     variance=work["variance"] if var else None)
         if ev is not None:
             ev[2].record(stream)
 
@@ -239,7 +243,7 @@ def main():
             scratch.fill_(float(i))
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record(stream)
-            plan.reassign(K, V, mu0, out=work)
+            plan.reassign(K, V, mu0, out=work, variance=var)
             ev[1].record(stream)
             torch.cuda.synchronize()
             flushed.append(ev[0].elapsed_time(ev[1]))
@@ -264,10 +268,10 @@ def main():
             evs_c = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
             for r in range(10):
                 evs_c[r][0].record(stream)
-                plan.reassign(Kd, Vd, cur_mu, out=work)
+                plan.reassign(Kd, Vd, cur_mu, out=work, variance=var)
                 evs_c[r][1].record(stream)
                 plan.forward(Q, Kd, Vd, work["centroids"], work["mean_values"], work["counts"],
-                             out=O_out)
+                             out=O_out, variance=work["variance"] if var else None)
                 evs_c[r][2].record(stream)
             torch.cuda.synchronize()
             rs = [e[0].elapsed_time(e[1]) for e in evs_c[5:]]
@@ -311,7 +315,7 @@ def main():
                    cfg.height, cfg.width], "head_dim": d, "block": B, "clusters": C,
                    "key_block": Skb, "exact_blocks_per_row": cfg.blocks_per_row,
                    "density": round(pairs / (nb * cfg.num_key_blocks), 4),
-                   "mask_heads": int(mask.shape[0]),
+                   "mask_heads": int(mask.shape[0]), "variance_corrected": var,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

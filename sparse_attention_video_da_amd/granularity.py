@@ -8,7 +8,8 @@ Attention (AB-Attention) abstract packs key/value blocks smaller than a tile int
 tensor-core tiles to refine the selection). The cache is 10 `da_reassign` Lloyd iterations
 from the seeds, refreshed per mask (the counts depend on it). Reported per S: the forward's
 relative L2 distance to dense softmax attention with cluster compensation and with the
-exact blocks alone (every count zero). Dense attention is the library's forward on a plan
+exact blocks alone (every count zero), and with the variance-corrected compensation
+(`da_reassign_var` / `da_forward_var`). Dense attention is the library's forward on a plan
 whose mask keeps every block exact. Everything runs through the C ABI on one GPU; the host
 only reduces the reported numbers.
 
@@ -87,18 +88,22 @@ def main(argv=None):
         plan = S.Plan(H, N, d, B, C, mask, dtype="bf16", key_block=kb)
         mu = seeds
         for _ in range(args.iters):
-            out = plan.reassign(K, V, mu)
+            out = plan.reassign(K, V, mu, variance=True)
             mu = out["centroids"]
         if o_dense is None:
             o_dense = dense.forward(Q, K, V, out["centroids"], out["mean_values"], zeros)
         o_comp = plan.forward(Q, K, V, out["centroids"], out["mean_values"], out["counts"])
         o_exact = plan.forward(Q, K, V, out["centroids"], out["mean_values"], zeros)
+        o_var = plan.forward(Q, K, V, out["centroids"], out["mean_values"], out["counts"],
+                             variance=out["variance"])
         torch.cuda.synchronize()
         row = {"key_block": kb, "exact_blocks_per_row": kcfg.blocks_per_row,
                "exact_key_fraction": round(float(mask.sum()) * kb / (nb * N), 5),
-               "err_compensated": rel(o_comp, o_dense), "err_exact_only": rel(o_exact, o_dense)}
+               "err_compensated": rel(o_comp, o_dense), "err_exact_only": rel(o_exact, o_dense),
+               "err_variance_corrected": rel(o_var, o_dense)}
         rows.append(row)
-        print(f"[granularity] S={kb}: rel-L2 to dense {row['err_compensated']:.4f} "
+        print(f"[granularity] S={kb}: rel-L2 to dense {row['err_compensated']:.4f}, "
+              f"variance-corrected {row['err_variance_corrected']:.4f} "
               f"(exact blocks alone {row['err_exact_only']:.4f})", file=sys.stderr, flush=True)
         plan.close()
     dense.close()
