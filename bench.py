@@ -319,7 +319,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel": f"fwd_bf16_kernel<{d},{B},{Skb}>" if
+                     "traffic": traffic, "kernel": f"fwd_bf16_kernel<{d},{B},{Skb},{str(var).lower()}>" if
                      cfg.dtype == "bf16" else f"fwd_f32_kernel<{d},{B}>",
                      "flops_per_launch": exact_flop,
                      "flops_basis": "exact-block MFMA work, 4*B*S*d per (query block, exact "
