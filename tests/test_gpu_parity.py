@@ -56,9 +56,10 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     torch = torch_mod()
     H, N, d, B, C, dtype = (cfgd[k] for k in ("H", "N", "d", "B", "C", "dtype"))
     S = cfgd.get("S") or B
+    scale = cfgd.get("scale", 0.0)
     heads = list(range(H)) if heads is None else heads
     say(f"[case] {what}: H={H} N={N} d={d} B={B} S={S} C={C} {dtype} exact={int(mask.sum())}")
-    plan = lib.Plan(H, N, d, B, C, mask, dtype=dtype, key_block=S)
+    plan = lib.Plan(H, N, d, B, C, mask, dtype=dtype, key_block=S, scale=scale)
     dev = {x: to_dev(L[x], dtype) for x in ("Q", "K", "V")}
     mu0 = to_dev(mu0_stored, dtype)
     L64 = _layer64(L, dtype)
@@ -103,7 +104,7 @@ def _run_case(lib, L, mu0_stored, mask, cfgd, what, check_reassign=True, heads=N
     for h in heads:
         ref_o, ref_lse = O.forward(L64["Q"][h], L64["K"][h], L64["V"][h], caches[h]["mu1"],
                                    caches[h]["vbar"], caches[h]["counts"], mask_h(h), B,
-                                   kblock=S,
+                                   kblock=S, scale=scale or None,
                                    kvar=kv32[h].astype(np.float64) if variance else None)
         got_all.append(o[h])
         want_all.append(ref_o)
@@ -298,6 +299,17 @@ def test_max_clusters(lib, S):
     mask = (np.random.default_rng(9).random((1, nb, nkb)) < 0.2).astype(np.uint8)
     _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype="bf16", S=S),
               f"max clusters C={C} S{S_}")
+
+
+@pytest.mark.parametrize("dtype,scale", [("bf16", 0.05), ("bf16", 0.3), ("f32", 0.05)])
+def test_custom_scale(lib, dtype, scale):
+    """A softmax scale other than 1/sqrt(d) given in the descriptor."""
+    H, N, d, B, C = 2, 700, 64, 64, 30
+    L, cache = _random_layer(1000 + int(scale * 100), H, N, d, dtype, C)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(13).random((1, nb, nb)) < 0.3).astype(np.uint8)
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype=dtype, scale=scale),
+              f"scale {scale} {dtype}")
 
 
 # ----------------------------------------------------------------- variance-corrected compensation
