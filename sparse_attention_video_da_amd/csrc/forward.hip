@@ -7,8 +7,10 @@
 // softmax (exp2 domain) absorbs every tile. Cluster tiles add a per-key logit bias
 // log2(n[b][c]) (-inf where n = 0), which in the natural-log domain is the ln-count weight
 // of the DecoupAttn abstract: each cluster stands in for the n of its keys left outside the
-// exact blocks. The bf16 kernel gives a workgroup two adjacent query blocks (their exact
-// lists merged); the fp32 kernel one query block.
+// exact blocks. Optionally (the variance-corrected kernels) each cluster logit also gains
+// scale^2 kvar_c ||q||^2 / 2, the second-order weight of a cluster whose keys spread with
+// variance kvar_c around its centroid. The bf16 kernel gives a workgroup two adjacent query
+// blocks (their exact lists merged); the fp32 kernel one query block.
 //
 // Work split (bf16): wave w handles 32 query rows. Scores are formed transposed,
 // S^T = K * Q^T, so every lane owns one query column and the row max / row sum need only
@@ -23,9 +25,10 @@ namespace da {
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 
-// XCD-aware order: hardware deals workgroup ids round-robin to the 8 XCDs; give each XCD a
-// contiguous range of (head, query block) so neighbouring query blocks, which share many
-// 3D-local key blocks, hit the same L2.
+// XCD-aware order (fp32 kernel; the bf16 kernel uses the plan's work-balanced split):
+// hardware deals workgroup ids round-robin to the 8 XCDs; give each XCD a contiguous range of
+// (head, query block) so neighbouring query blocks, which share many 3D-local key blocks,
+// hit the same L2.
 __device__ __forceinline__ int xcd_remap(int L, int total) {
   int per = (total + 7) >> 3;
   return (L & 7) * per + (L >> 3);
@@ -36,8 +39,8 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
 // block. It walks the union of the two exact lists, so a key block both blocks keep exact
 // is fetched once (neighbouring query blocks of a 3D-local mask share most of their key
 // blocks), then the cluster tiles, which both blocks use with their own bias rows. An
-// exact tile holds G = BLK/S consecutive list entries; with G > 1 the list puts the key
-// blocks both query blocks use first, so nearly every tile serves one set of users. A wave
+// exact tile holds G = BLK/S consecutive list entries; with G > 1 each tile holds key blocks
+// of one set of users (both query blocks, or one of them), the tiles ascending by key. A wave
 // skips the tiles that hold no key of its block, and the bias row of the tile masks the
 // key blocks of a mixed tile that its block does not keep.
 struct TileDesc {

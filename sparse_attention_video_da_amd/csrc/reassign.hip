@@ -15,7 +15,9 @@
 //                    every cluster's keys sit contiguously in ascending key order.
 //   6. sums          fixed-size segments of the sorted order give fp32 partial sums per
 //                    cluster run, then one wave per cluster adds its partials in order,
-//                    divides and rounds to the cache dtype (deterministic throughout).
+//                    divides and rounds to the cache dtype (deterministic throughout); with
+//                    the key variance requested, the squared key norms ride along and the
+//                    finish writes each cluster's isotropic key variance.
 //   7. counts        n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c], per pair
 //                    (with key blocks smaller than the query blocks: size[c] minus the
 //                    exact keys of cluster c, read from the assignments).
