@@ -22,6 +22,26 @@
 
 namespace da {
 
+// Schedule of the bf16 kernel's pipelined chunk loop (overridable at build time; a sweep on
+// the 13B-class layer left these values best): KC 32-key subtiles per softmax chunk; per MFMA
+// of a chunk, NV VALU instructions and ND LDS reads beside it; NPRE LDS reads issued ahead of a
+// chunk's first MFMA, and Q0PRE ahead of the first chunk of a tile.
+#ifndef FWD_KC
+#define FWD_KC 2
+#endif
+#ifndef FWD_NV
+#define FWD_NV 5
+#endif
+#ifndef FWD_ND
+#define FWD_ND 2
+#endif
+#ifndef FWD_NPRE
+#define FWD_NPRE 8
+#endif
+#ifndef FWD_Q0PRE
+#define FWD_Q0PRE 12
+#endif
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -129,21 +149,6 @@ fwd_bf16_kernel(FwdArgs p) {
   constexpr int PER_T = (BLK * NCH) / THREADS;   // 16-byte fetches per thread per tensor
   static_assert(PER_T * THREADS == BLK * NCH, "tile must split evenly");
   constexpr float kSumLimit = 32768.f;   // partial row sum that forces a max update
-#ifndef FWD_KC
-#define FWD_KC 2
-#endif
-#ifndef FWD_NV
-#define FWD_NV 5
-#endif
-#ifndef FWD_ND
-#define FWD_ND 2
-#endif
-#ifndef FWD_NPRE
-#define FWD_NPRE 8
-#endif
-#ifndef FWD_Q0PRE
-#define FWD_Q0PRE 12
-#endif
   constexpr int KC = FWD_KC;       // 32-key subtiles per softmax chunk
 
   // Two LDS stages, each stage's K and V tiles a separate object: with the stage chosen
