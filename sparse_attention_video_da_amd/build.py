@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdecoupattn.so")
-SOURCES = ["api.cpp", "forward.hip", "reassign.hip"]
+SOURCES = ["api.cpp", "plan_lists.cpp", "forward.hip", "reassign.hip"]
 ARCH = "gfx950"
 
 COMMON = [

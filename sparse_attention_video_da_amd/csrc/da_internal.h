@@ -4,15 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace da {
+#include "plan_lists.h"
 
-// Pair-list entry: key block index | used by query block 2p | used by 2p+1 | the key block
-// runs past N. With G = B/S key blocks per tile (S < B) a pair's list is a sequence of
-// G-entry tiles, each holding key blocks of one set of users (both, only 2p, only 2p+1),
-// ascending by first key block; padding entries repeat a set's last entry with its use
-// bits clear.
-constexpr int32_t kEntIndex = 0x0fffffff;
-constexpr int kEntUse0 = 28, kEntUse1 = 29, kEntPartial = 30;
+namespace da {
 
 // Everything the fused forward kernel reads, in device memory.
 struct FwdArgs {
