@@ -110,3 +110,17 @@ def test_positional_locality_is_a_distance_kernel_and_off_by_default():
     assert all((a[k] == b[k]).all() for k in ("Q", "K", "V"))
     c = head_tensors(cfg, 1)
     assert (c["V"] == a["V"]).all() and not (c["K"] == a["K"]).all()
+
+
+def test_generator_is_deterministic_and_per_head():
+    """Same seed, same bytes; a head generated alone equals that head of the whole layer."""
+    from datagen import make_layer
+    cfg = get_config("small_bf16")
+    a = make_layer(cfg, threads=2)
+    b = make_layer(cfg, threads=8)
+    for k in ("Q", "K", "V", "mask", "cache_init"):
+        assert np.array_equal(a[k], b[k]), k
+    one = make_layer(cfg, heads=[5], threads=1)
+    for k in ("Q", "K", "V", "cache_init"):
+        assert np.array_equal(one[k][0], a[k][5]), k
+    assert not np.array_equal(a["K"][4], a["K"][5])       # heads draw their own streams

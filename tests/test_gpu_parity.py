@@ -355,6 +355,99 @@ def test_zero_variance_equals_plain_forward(lib):
     plan.close()
 
 
+# ----------------------------------------------------------------- invariants on the GPU
+def _dev_run(lib, L, cache, mask, H, N, d, B, C, counts=None, lse=True):
+    torch = torch_mod()
+    plan = lib.Plan(H, N, d, B, C, mask)
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], to_dev(cache, "bf16"))
+    cnt = out["counts"] if counts is None else counts
+    o, l = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"], out["mean_values"], cnt,
+                        lse=lse)
+    torch.cuda.synchronize()
+    res = {k: v.cpu() for k, v in out.items()}
+    res["O"] = from_dev(o, "bf16")
+    res["lse"] = l.cpu().numpy().astype(np.float64)
+    plan.close()
+    return res
+
+
+def test_cluster_constant_layer_is_dense(lib):
+    """Every key of a cluster equal to its centroid, every value of it equal: the compensation
+    is exact, so any mask gives dense attention."""
+    H, N, d, B, C = 2, 900, 128, 128, 12
+    rng = np.random.default_rng(31)
+    from datagen import f32_to_bf16_bits
+    L = {}
+    cache = []
+    lab = rng.integers(0, C, (H, N))
+    keys = rng.standard_normal((H, C, d)).astype(np.float32)
+    vals = rng.standard_normal((H, C, d)).astype(np.float32)
+    L["K"] = f32_to_bf16_bits(np.stack([keys[h][lab[h]] for h in range(H)]))
+    L["V"] = f32_to_bf16_bits(np.stack([vals[h][lab[h]] for h in range(H)]))
+    L["Q"] = f32_to_bf16_bits(rng.standard_normal((H, N, d)).astype(np.float32))
+    cache = f32_to_bf16_bits(keys)
+    nb = -(-N // B)
+    mask = (rng.random((1, nb, nb)) < 0.3).astype(np.uint8)
+    r = _dev_run(lib, L, cache, mask, H, N, d, B, C)
+    L64 = _layer64(L, "bf16")
+    for h in range(H):
+        want = O.dense_attention(L64["Q"][h], L64["K"][h], L64["V"][h])
+        check_forward(r["O"][h], want, "bf16", f"cluster-constant head {h} vs dense")
+
+
+def test_convexity_and_lse_merge_on_gpu(lib):
+    """Outputs lie within each dimension's value range; the exact-only and compensation-only
+    forwards (counts zeroed; mask emptied) merged by their log-sum-exps give the full one."""
+    torch = torch_mod()
+    H, N, d, B, C = 2, 1000, 128, 128, 40
+    L, cache = _random_layer(32, H, N, d, "bf16", C)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(33).random((1, nb, nb)) < 0.35).astype(np.uint8)
+    mask[0, :, 0] = 1                      # every block keeps one exact block (finite lse)
+    full = _dev_run(lib, L, cache, mask, H, N, d, B, C)
+    V64 = _layer64(L, "bf16")["V"]
+    lo, hi = V64.min(axis=1, keepdims=True), V64.max(axis=1, keepdims=True)
+    assert np.all(full["O"] >= lo - 2e-2) and np.all(full["O"] <= hi + 2e-2)
+    zero = torch.zeros((H, nb, C), dtype=torch.int32, device="cuda")
+    ex = _dev_run(lib, L, cache, mask, H, N, d, B, C, counts=zero)
+    cp = _dev_run(lib, L, cache, np.zeros_like(mask), H, N, d, B, C,
+                  counts=full["counts"].cuda())
+    we = np.exp(ex["lse"] - full["lse"])
+    wc = np.exp(cp["lse"] - full["lse"])
+    assert np.max(np.abs(we + wc - 1.0)) < 1e-2
+    merged = ex["O"] * we[..., None] + cp["O"] * wc[..., None]
+    check_forward(merged.reshape(-1, d), full["O"].reshape(-1, d), "bf16", "lse merge")
+
+
+def test_label_permutation_on_gpu(lib):
+    """Reordering the cached centroids relabels the clusters: assignments, sizes, counts and
+    means follow the permutation, and the output does not change."""
+    H, N, d, B, C = 2, 1000, 128, 128, 40
+    L, cache = _random_layer(34, H, N, d, "bf16", C)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(35).random((1, nb, nb)) < 0.3).astype(np.uint8)
+    perm = np.random.default_rng(36).permutation(C)
+    a = _dev_run(lib, L, cache, mask, H, N, d, B, C)
+    b = _dev_run(lib, L, np.ascontiguousarray(cache[:, perm]), mask, H, N, d, B, C)
+    inv = np.argsort(perm)
+    L64 = _layer64(L, "bf16")
+    band = False
+    for h in range(H):
+        # key j assigned to cluster c in run a is assigned to inv[c] in run b, except where
+        # the two nearest centroids sit inside the tie band (either choice is allowed there)
+        gap = O.assign(L64["K"][h], O.to_f64(cache[h], "bf16"))[1]
+        sure = gap >= O.TIE_BAND
+        band |= bool((~sure).any())
+        assert np.array_equal(inv[a["assign"][h].numpy()][sure], b["assign"][h].numpy()[sure])
+    if not band:
+        assert np.array_equal(a["sizes"].numpy()[:, perm], b["sizes"].numpy())
+        assert np.array_equal(a["counts"].numpy()[:, :, perm], b["counts"].numpy())
+        assert np.array_equal(a["centroids"].view(torch_mod().int16).numpy()[:, perm],
+                              b["centroids"].view(torch_mod().int16).numpy())
+    check_forward(b["O"].reshape(-1, d), a["O"].reshape(-1, d), "bf16", "permuted labels")
+
+
 def test_all_blocks_exact_is_dense(lib):
     """Every block exact: the GPU output is dense attention (oracle's dense routine)."""
     torch = torch_mod()
