@@ -60,7 +60,8 @@ typedef enum { DA_DTYPE_F32 = 0, DA_DTYPE_BF16 = 1 } da_dtype;
 
 /* Shape of one attention layer.
  *   heads       H >= 1
- *   seq_len     N >= 1 tokens per head
+ *   seq_len     N >= 1 tokens per head, with N * d * (element bytes) < 2^31 (one head's Q, K,
+ *               V or O addressed with 32-bit byte offsets)
  *   head_dim    d in {64, 128}
  *   block       B in {64, 128}: query block size of the mask (and the tile height)
  *   clusters    C, 1 <= C <= N and C <= 8192

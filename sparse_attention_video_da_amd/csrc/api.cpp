@@ -80,10 +80,12 @@ da_status check_desc(const da_desc* d) {
   if (d->key_block < 0) return DA_ERR_INVALID_ARGUMENT;
   const int32_t S = key_block_of(*d);
   if ((S != 16 && S != 32 && S != 64 && S != 128) || S > d->block) return DA_ERR_UNSUPPORTED;
-  // int32 indexing of [H][N][d] element offsets, [H][nb][C] counts and the mask
+  // int32 byte offsets within one head's [N][d] tensor (the kernels' buffer resources and
+  // row offsets), int32 indexing of [H][nb][C] counts and of the mask
   const int64_t nb = (d->seq_len + d->block - 1) / d->block;
   const int64_t nkb = (d->seq_len + S - 1) / S;
-  if ((int64_t)d->seq_len * d->head_dim > INT32_MAX || nb * d->clusters > INT32_MAX ||
+  const int64_t es = d->dtype == DA_DTYPE_BF16 ? 2 : 4;
+  if ((int64_t)d->seq_len * d->head_dim * es > INT32_MAX || nb * d->clusters > INT32_MAX ||
       nb * nkb * d->mask_heads > INT32_MAX)
     return DA_ERR_UNSUPPORTED;
   return DA_OK;

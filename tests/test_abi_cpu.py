@@ -66,6 +66,15 @@ def test_key_block_above_query_block_is_unsupported(S):
     assert S.da_validate_desc(d, _ok_mask()) == S.DA_OK
 
 
+def test_per_head_byte_size_limit(S):
+    """One head's [N][d] tensor must be addressable with 32-bit byte offsets. (For bf16 the
+    mask's nb x nkb limit binds first; fp32 at d = 128 reaches the byte limit.)"""
+    d = S.make_desc(1, 4_194_304, 128, 128, 16, dtype="f32")   # exactly 2^31 bytes
+    assert S.da_validate_desc(d, _ok_mask()) == S.DA_ERR_UNSUPPORTED
+    d.seq_len = 4_194_303
+    assert S.da_validate_desc(d, _ok_mask()) == S.DA_OK
+
+
 def test_validation_rejects_null_mask_and_desc(S):
     d = S.make_desc(2, 1000, 128, 128, 16)
     assert S.da_validate_desc(d, None) == S.DA_ERR_INVALID_ARGUMENT
