@@ -31,6 +31,9 @@
  *     caller's next synchronisation. The library never prints and never throws.
  *   - A plan owns a device workspace; one plan must not be used by two streams at once.
  *     Distinct plans are independent.
+ *   - A plan belongs to the device that was current when it was created: compute entry
+ *     points must be called with that device current, and a non-NULL stream must be one of
+ *     its streams (checked; INVALID_ARGUMENT otherwise).
  */
 #ifndef DECOUPATTN_H
 #define DECOUPATTN_H
@@ -102,7 +105,8 @@ typedef struct da_plan_s* da_plan;
 DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* block_mask_host,
                                 da_plan* out);
 
-/* Release a plan and its device memory (synchronises the device first). NULL is a no-op. */
+/* Release a plan and its device memory (synchronises the plan's device first; the caller's
+ * current device is left as it was). NULL is a no-op. */
 DA_API da_status da_plan_destroy(da_plan plan);
 
 /* Reassign Cache step (abstract: each step reassigns drifted keys to the cached

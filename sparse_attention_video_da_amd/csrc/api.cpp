@@ -101,8 +101,36 @@ void destroy_device(da_plan_s* p) {
   p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = p->d_part = p->d_psq = nullptr;
 }
 
-std::once_flag g_prep_once;
-hipError_t g_prep_err = hipSuccess;
+// Kernel attributes (dynamic LDS limits) are set once per device, on first use.
+std::mutex g_prep_mu;
+std::vector<int> g_prepared;
+
+hipError_t prepare_device(int dev) {
+  std::lock_guard<std::mutex> lock(g_prep_mu);
+  for (int x : g_prepared)
+    if (x == dev) return hipSuccess;
+  hipError_t e = da::prepare_forward_kernels();
+  if (e == hipSuccess) e = da::prepare_reassign_kernels();
+  if (e == hipSuccess) g_prepared.push_back(dev);
+  return e;
+}
+
+// A plan's lists and workspace live on the device that was current at its creation: compute
+// calls must run with that device current and, when a stream is given, on one of its streams.
+da_status check_device(const da_plan_s* p, void* stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DA_ERR_DEVICE;
+  if (dev != p->device) return DA_ERR_INVALID_ARGUMENT;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return DA_ERR_INVALID_ARGUMENT;
+    }
+    if (sdev != p->device) return DA_ERR_INVALID_ARGUMENT;
+  }
+  return DA_OK;
+}
 
 }  // namespace
 
@@ -162,11 +190,8 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
     delete p;
     return DA_ERR_DEVICE;
   }
-  std::call_once(g_prep_once, [] {
-    g_prep_err = da::prepare_forward_kernels();
-    if (g_prep_err == hipSuccess) g_prep_err = da::prepare_reassign_kernels();
-  });
-  if (g_prep_err != hipSuccess) {
+  if (prepare_device(p->device) != hipSuccess) {
+    (void)hipGetLastError();
     delete p;
     return DA_ERR_DEVICE;
   }
@@ -208,8 +233,13 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
 
 DA_API da_status da_plan_destroy(da_plan p) {
   if (p == nullptr) return DA_OK;
+  // synchronise and free on the plan's device, leaving the caller's current device as it was
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  const bool switched = have_cur && cur != p->device && hipSetDevice(p->device) == hipSuccess;
   (void)hipDeviceSynchronize();
   destroy_device(p);
+  if (switched) (void)hipSetDevice(cur);
   delete p;
   return DA_OK;
 }
@@ -247,6 +277,7 @@ da_status reassign_impl(da_plan p, const void* K, const void* V, const void* cen
       cluster_sizes_out == nullptr || qblock_counts_out == nullptr ||
       (want_variance && key_variance_out == nullptr))
     return DA_ERR_INVALID_ARGUMENT;
+  if (const da_status ds = check_device(p, stream); ds != DA_OK) return ds;
   const da_desc& d = p->desc;
   const size_t es = elem_size(d);
   const size_t cache_bytes = (size_t)d.heads * d.clusters * d.head_dim * es;
@@ -310,6 +341,7 @@ da_status forward_impl(da_plan p, const void* Q, const void* K, const void* V,
       (lse_out != nullptr && !aligned(lse_out, 4)) ||
       (want_variance && !aligned(key_variance, 4)))
     return DA_ERR_INVALID_ARGUMENT;
+  if (const da_status ds = check_device(p, stream); ds != DA_OK) return ds;
   const da_desc& d = p->desc;
   da::FwdArgs a{};
   a.Q = Q;

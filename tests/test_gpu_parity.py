@@ -540,3 +540,35 @@ def test_entry_point_validation_on_device(lib):
                         mu.data_ptr(), outs[3].data_ptr(), K.data_ptr(), None, None)
     assert st == lib.DA_ERR_INVALID_ARGUMENT
     plan.close()
+
+
+def test_side_stream_matches_current_stream(lib):
+    """A plan driven on a side stream (the library checks that the stream belongs to the
+    plan's device) gives bit-identical results to the same step on the current stream: every
+    kernel is deterministic."""
+    torch = torch_mod()
+    H, N, d, B, C = 2, 1000, 128, 128, 40
+    L, cache = _random_layer(31, H, N, d, "bf16", C)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(31).random((1, nb, nb)) < 0.3).astype(np.uint8)
+    plan = lib.Plan(H, N, d, B, C, mask)
+    dev = {x: to_dev(L[x], "bf16") for x in ("Q", "K", "V")}
+    mu0 = to_dev(cache, "bf16")
+
+    def step(stream):
+        out = plan.reassign(dev["K"], dev["V"], mu0, stream=stream)
+        o, lse = plan.forward(dev["Q"], dev["K"], dev["V"], out["centroids"],
+                              out["mean_values"], out["counts"], lse=True, stream=stream)
+        return out, o, lse
+
+    ref = step(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = step(side)
+    side.synchronize()
+    for k in ("centroids", "mean_values", "assign", "sizes", "counts"):
+        assert torch.equal(ref[0][k], got[0][k]), k
+    assert torch.equal(ref[1], got[1]) and torch.equal(ref[2], got[2])
+    plan.close()
