@@ -191,12 +191,10 @@ CONFIGS: Dict[str, LayerConfig] = {
                     "drift with reassign + forward"),
 }
 
-ALIASES = {"C1": "tiny_f32", "C2": "small_bf16", "C3": "wan14b_bf16",
-           "C4": "hunyuan13b_bf16", "C5": "extreme_cache_bf16"}
-
-
 def get_config(name: str) -> LayerConfig:
-    return CONFIGS[ALIASES.get(name, name)]
+    if name not in CONFIGS:
+        raise KeyError(f"unknown workload {name!r}; known: {', '.join(CONFIGS)}")
+    return CONFIGS[name]
 
 
 def _rng(cfg: LayerConfig, head: int, stream: int, step: int = 0) -> np.random.Generator:
