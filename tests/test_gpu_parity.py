@@ -572,3 +572,51 @@ def test_side_stream_matches_current_stream(lib):
         assert torch.equal(ref[0][k], got[0][k]), k
     assert torch.equal(ref[1], got[1]) and torch.equal(ref[2], got[2])
     plan.close()
+
+
+def test_layer_step_replays_in_a_hip_graph(lib):
+    """The compute calls enqueue kernels only (no allocation, memset or synchronisation), so a
+    layer step (reassign + forward) can be captured in a HIP graph. Every replay, with eager
+    work and synchronisation between replays, is bit-identical to the eager step."""
+    torch = torch_mod()
+    H, N, d, B, C = 2, 1000, 128, 128, 40
+    L, cache = _random_layer(41, H, N, d, "bf16", C)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(41).random((1, nb, nb)) < 0.3).astype(np.uint8)
+    plan = lib.Plan(H, N, d, B, C, mask)
+    Q, K, V = (to_dev(L[x], "bf16") for x in ("Q", "K", "V"))
+    mu0 = to_dev(cache, "bf16")
+    out = plan.reassign(K, V, mu0)
+    O = torch.empty_like(Q)
+
+    def step(s=None):
+        plan.reassign(K, V, mu0, out=out, stream=s)
+        plan.forward(Q, K, V, out["centroids"], out["mean_values"], out["counts"], out=O,
+                     stream=s)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    ref_o = O.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for v in out.values():
+            v.zero_()
+        O.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(ref[k], out[k]), (r, k)
+        assert torch.equal(ref_o, O), r
+        step()
+        torch.cuda.synchronize()
+    del graph
+    plan.close()
