@@ -148,7 +148,12 @@ fwd_bf16_kernel(FwdArgs p) {
   constexpr int TILE = BLK * D * 2;
   constexpr int PER_T = (BLK * NCH) / THREADS;   // 16-byte fetches per thread per tensor
   static_assert(PER_T * THREADS == BLK * NCH, "tile must split evenly");
-  constexpr float kSumLimit = 32768.f;   // partial row sum that forces a max update
+  // Partial row sum (one lane's 32 probabilities of a chunk) that forces a max update. With
+  // probabilities kept at most 2^30, a row sum over thousands of chunks stays below 2^43 and O
+  // below 2^43 max|v|, far inside fp32; bf16 and fp32 keep their relative precision at any
+  // magnitude. (A limit of 2^15 made the cluster tiles, whose log-count biases lift their
+  // probabilities, rescale often: 3% of the forward at 5% density, 9% at 1%.)
+  constexpr float kSumLimit = 1073741824.f;
   constexpr int KC = FWD_KC;       // 32-key subtiles per softmax chunk
 
   // Two LDS stages, each stage's K and V tiles a separate object: with the stage chosen
@@ -508,10 +513,10 @@ fwd_bf16_kernel(FwdArgs p) {
         float lsum = exp_pack(sc, pc);
         interleave_mfma_valu<16 * KC, FWD_NV, FWD_ND, FWD_NPRE>();
         // The reference max moves only when some row's probabilities outgrow it (a partial
-        // row sum above 2^15, or inf on the first tile); then the chunk's true max is taken,
+        // row sum above 2^30, or inf on the first tile); then the chunk's true max is taken,
         // O (including the PV of chunk c-1, computed at the old max) and l are rescaled and
         // the chunk is recomputed. Otherwise probabilities may exceed 1 (each at most
-        // 2^15), which fp32 and bf16 carry.
+        // 2^30), which fp32 and bf16 carry.
         if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit)) != 0) {
           float mx = kNegInf;
 #pragma unroll
