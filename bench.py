@@ -155,7 +155,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the per-head "
               "decomposition shards across GPUs without communication, but no multi-GPU "
-              "figure is produced by this build.", file=sys.stderr)
+              "figure is measured here.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
