@@ -183,6 +183,12 @@ CONFIGS: Dict[str, LayerConfig] = {
         local_rule="reach",
         description="13B-class layer with exact key blocks of 64 keys: the 92 nearest to "
                     "some token of each query block of 128 (5% of keys)"),
+    "long_video_bf16": LayerConfig(
+        "long_video_bf16", 13, heads=1, frames=129, height=72, width=111, head_dim=128,
+        block=128, clusters=512, mask_kind="local", blocks_per_row=46, first_frame=False,
+        mixture=256, sigma=0.25, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        description="1 head, N=1030968 (129x72x111, a ragged last block of 56), d=128, "
+                    "block 128, C=512, 46 3D-local blocks per query block (0.57%)"),
     "extreme_cache_bf16": LayerConfig(
         "extreme_cache_bf16", 5, heads=40, frames=21, height=45, width=80, head_dim=128,
         block=128, clusters=512, mask_kind="local", blocks_per_row=6, first_frame=False,

@@ -132,3 +132,48 @@ def test_extreme_cache_four_steps(lib, pool):
         L = drift_layer(cfg, L, step, threads=16)
         mu = _step(lib, plan, cfg, L, mu, step + 1, pool, qblocks, f"extreme step {step}")
     plan.close()
+
+
+def test_long_sequence_layer(lib):
+    """One head of about a million tokens (8055 query blocks, a ragged last block of 56): the
+    plan's lists, the counting sort and the forward's grid at that length. The oracle assigns
+    and refreshes every key, and takes the counts of 16 sampled query blocks (always the first
+    and the ragged last) by the direct count; the GPU forward is then teacher-forced with the
+    oracle's cache and those count rows (zeros elsewhere) and checked on the sampled blocks."""
+    torch = torch_mod()
+    cfg = get_config("long_video_bf16")
+    dt, N, d, B, C = cfg.dtype, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters
+    nb = cfg.num_blocks
+    L = make_layer(cfg, threads=16)
+    mask = L["mask"][0]
+    say(f"[case] long sequence: N={N} nb={nb} C={C} exact={int(mask.sum())}")
+    plan = lib.Plan(1, N, d, B, C, L["mask"], dtype=dt)
+    dev = {x: to_dev(L[x], dt) for x in ("Q", "K", "V")}
+    out = plan.reassign(dev["K"], dev["V"], to_dev(L["cache_init"], dt))
+    torch.cuda.synchronize()
+    qb = _sample_qblocks(cfg, 16, 17)
+    K64 = O.to_f64(L["K"][0], dt)
+    V64 = O.to_f64(L["V"][0], dt)
+    mu0 = O.to_f64(L["cache_init"][0], dt)
+    a, gap, d1, d2 = O.assign(K64, mu0)
+    ref = O.refresh(K64, V64, a, mu0, mask[qb], B, dt)
+    ref.update(assign=a, gap=gap, d1=d1, d2=d2)
+    say("  oracle reassign done")
+    gpu = {"assign": out["assign"][0].cpu().numpy(), "sizes": out["sizes"][0].cpu().numpy(),
+           "counts": out["counts"][0].cpu().numpy()[qb],
+           "centroids": from_dev(out["centroids"][0], dt),
+           "mean_values": from_dev(out["mean_values"][0], dt)}
+    r = check_reassign_head(K64, None, mu0, mask[qb], B, dt, gpu, "long sequence", ref=ref)
+    say(f"  reassign ok ({r['band_moves']} in-band moves)")
+    cnt = np.zeros((1, nb, C), np.int32)
+    cnt[0, qb] = ref["counts"]
+    o = plan.forward(dev["Q"], dev["K"], dev["V"], to_dev(store64(ref["mu1"], dt)[None], dt),
+                     to_dev(store64(ref["vbar"], dt)[None], dt), torch.from_numpy(cnt).cuda())
+    torch.cuda.synchronize()
+    cnt64 = cnt[0].astype(np.int64)
+    want, _ = O.forward(O.to_f64(L["Q"][0], dt), K64, V64, ref["mu1"], ref["vbar"], cnt64, mask,
+                        B, qblocks=qb)
+    rows = rows_of(qb, B, N)
+    check_forward(from_dev(o[0][torch.from_numpy(rows).cuda()], dt), want[rows], dt,
+                  f"long sequence forward ({len(qb)} blocks)")
+    plan.close()
