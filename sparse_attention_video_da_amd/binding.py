@@ -207,6 +207,13 @@ class Plan:
             da_plan_destroy(self._h)
             self._h = None
 
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
+
     def __del__(self):
         try:
             self.close()
@@ -223,6 +230,9 @@ class Plan:
         dtype = self._tdtype() if dtype is None else dtype
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a device tensor")
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name} is on {t.device}, but the current device is "
+                             f"cuda:{torch.cuda.current_device()} (the plan's device)")
         if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
             raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
                              f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")

@@ -658,3 +658,21 @@ def test_wide_logit_range_moves_the_reference_max(lib, d, B, S, dtype):
     mask[0, 1, :] = 0
     _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype=dtype, S=S),
               f"wide logits d{d} B{B} S{S} {dtype}")
+
+
+def test_plan_as_context_manager_and_after_close(lib):
+    """`with Plan(...)` releases the plan on exit; a closed plan's calls raise (the library
+    rejects the null handle before enqueuing anything)."""
+    torch = torch_mod()
+    H, N, d, B, C = 1, 300, 64, 64, 8
+    L, cache = _random_layer(51, H, N, d, "bf16", C)
+    mask = np.ones((1, 5, 5), np.uint8)
+    K = to_dev(L["K"], "bf16")
+    with lib.Plan(H, N, d, B, C, mask) as plan:
+        out = plan.reassign(K, K, to_dev(cache, "bf16"))
+        torch.cuda.synchronize()
+        assert int(out["sizes"].sum().item()) == H * N
+    assert plan._h is None
+    with pytest.raises(lib.DAError):
+        plan.reassign(K, K, to_dev(cache, "bf16"))
+    plan.close()   # a second close is a no-op
