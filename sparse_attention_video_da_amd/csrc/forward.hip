@@ -72,6 +72,12 @@ struct TileDesc {
   int partial;     // exact tile: one of its key blocks runs past N
 };
 
+// A compile-time int passed to a generic lambda.
+template <int N>
+struct ic {
+  static constexpr int value = N;
+};
+
 // Read-only, wave-uniform loads through the scalar cache.
 __device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
   return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
@@ -91,8 +97,11 @@ __device__ __forceinline__ int pick(ents_t en, int first, int j) {
   return v;
 }
 
-template <int D, int BLK, int G>
-__device__ __forceinline__ TileDesc tile_desc(int t, int n_ex, ents_t en, int C) {
+// Tiles t < n_ex are exact, the rest cluster tiles; with PH (the variance-corrected kernels)
+// the first nd (0 or 1) tiles after the exact ones are a placeholder every wave skips, which
+// evens the exact count.
+template <int D, int BLK, int G, bool PH>
+__device__ __forceinline__ TileDesc tile_desc(int t, int n_ex, int nd, ents_t en, int C) {
   TileDesc d;
   if (t < n_ex) {
     int u = 0;
@@ -105,12 +114,12 @@ __device__ __forceinline__ TileDesc tile_desc(int t, int n_ex, ents_t en, int C)
     d.use = (u >> kEntUse0) & 3;
     d.partial = (u >> kEntPartial) & 1;
   } else {
-    const int ct = t - n_ex;
+    const int ct = PH ? max(t - n_ex - nd, 0) : t - n_ex;
     d.c0 = ct * BLK;
     d.off = d.c0 * D * 2;
     d.valid = min(BLK, C - d.c0);
     d.kind = 2;
-    d.use = 3;
+    d.use = (PH && t < n_ex + nd) ? 0 : 3;
     d.partial = 0;
   }
   return d;
@@ -198,7 +207,11 @@ fwd_bf16_kernel(FwdArgs p) {
   const int mh = p.mask_heads == 1 ? 0 : h;
   const int e0 = sload(p.prowptr, mh * (p.npairs + 1) + pr);
   const int n_ex = (sload(p.prowptr, mh * (p.npairs + 1) + pr + 1) - e0) / G;   // exact tiles
-  const int ntiles = n_ex + (p.C + BLK - 1) / BLK;
+  // VARC: the exact tiles run the plain score initialisation (their correction row is 0) and
+  // the cluster tiles the corrected one, as two loops over static stages; a placeholder tile
+  // evens an odd exact count so the cluster loop starts on stage 0
+  const int nd = VARC ? (n_ex & 1) : 0;
+  const int ntiles = n_ex + nd + (p.C + BLK - 1) / BLK;
 
   // Direct-to-LDS fetch of one K or V tile: the lane filling physical LDS slot (row, pc)
   // reads logical chunk pc ^ swz_key(row); each wave instruction fills 1 KB of consecutive
@@ -346,7 +359,7 @@ fwd_bf16_kernel(FwdArgs p) {
 
   // prologue: tile 0 into stage 0
   ents_t en = load_entries(0);   // entries of the tile being prefetched
-  TileDesc cur = tile_desc<D, BLK, G>(0, n_ex, en, p.C);
+  TileDesc cur = tile_desc<D, BLK, G, VARC>(0, n_ex, nd, en, p.C);
   fetch_tile(cur, en, k_s0, v_s0);
   if (bias_owner) bias_s0[tid] = bias_of(cur, en, load_count(cur));
   if constexpr (VARC) {
@@ -397,14 +410,16 @@ fwd_bf16_kernel(FwdArgs p) {
   __syncthreads();
 
   // one tile: compute on (k_lds, v_lds, bias_cur) while tile t+1 streams into (nk, nv)
-  auto tile = [&](int t, const char* k_lds, const char* v_lds, const float* bias_cur,
+  // VN: this tile runs the variance-corrected score initialisation
+  auto tile = [&](auto vn, int t, const char* k_lds, const char* v_lds, const float* bias_cur,
                   const float* w_cur, char* nk, char* nv, float* bias_nxt, float* w_nxt) {
+    constexpr bool VN = VARC && decltype(vn)::value != 0;
     const float* bias_lds = bias_cur + half * BLK;
     const float* w_lds = w_cur + half * BLK;
 
     // prefetch tile t+1 into the other stage (free since the barrier closing tile t-1)
     const bool has_next = t + 1 < ntiles;
-    const TileDesc nxt = tile_desc<D, BLK, G>(t + 1, n_ex, en, p.C);
+    const TileDesc nxt = tile_desc<D, BLK, G, VARC>(t + 1, n_ex, nd, en, p.C);
     int cnt_next = 0;
     float w_next = 0.f;
     if (has_next) {
@@ -442,7 +457,7 @@ fwd_bf16_kernel(FwdArgs p) {
           for (int i = 0; i < 4; ++i) {
             const f32x4 bv = *reinterpret_cast<const f32x4*>(
                 bias_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
-            if constexpr (VARC) {
+            if constexpr (VN) {
               const f32x4 wv = *reinterpret_cast<const f32x4*>(
                   w_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
 #pragma unroll
@@ -550,9 +565,23 @@ fwd_bf16_kernel(FwdArgs p) {
     __syncthreads();
     cur = nxt;
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
-    if (t + 1 < ntiles) tile(t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+  if constexpr (VARC) {
+    int t = 0;
+    for (; t < n_ex + nd; t += 2) {   // an even count
+      tile(ic<0>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+      tile(ic<0>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+    }
+    for (; t < ntiles; t += 2) {
+      tile(ic<1>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+      if (t + 1 < ntiles)
+        tile(ic<1>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+    }
+  } else {
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(ic<0>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+      if (t + 1 < ntiles)
+        tile(ic<0>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+    }
   }
 
   // Epilogue: normalise and store. Lane holds O[q][32dt + 8i + 4hl + j].
