@@ -410,10 +410,12 @@ fwd_bf16_kernel(FwdArgs p) {
   __syncthreads();
 
   // one tile: compute on (k_lds, v_lds, bias_cur) while tile t+1 streams into (nk, nv)
-  // VN: this tile runs the variance-corrected score initialisation
-  auto tile = [&](auto vn, int t, const char* k_lds, const char* v_lds, const float* bias_cur,
+  // Score initialisation of this tile: mode 0 from the bias row, 1 from the bias and
+  // variance rows (VARC), 2 zero (an exact tile whose bias row is all zero)
+  auto tile = [&](auto mode, int t, const char* k_lds, const char* v_lds, const float* bias_cur,
                   const float* w_cur, char* nk, char* nv, float* bias_nxt, float* w_nxt) {
-    constexpr bool VN = VARC && decltype(vn)::value != 0;
+    constexpr bool VN = VARC && decltype(mode)::value == 1;
+    constexpr bool ZI = decltype(mode)::value == 2;
     const float* bias_lds = bias_cur + half * BLK;
     const float* w_lds = w_cur + half * BLK;
 
@@ -449,12 +451,18 @@ fwd_bf16_kernel(FwdArgs p) {
       bf16x8 pk[2][KC][2];
       // Scores start from the tile's bias row (0 for a kept key, -inf for a key past N or of
       // a key block the query block does not keep, and log2 of the outside count for a
-      // cluster tile, all divided by the scale).
+      // cluster tile, all divided by the scale), or from zero in a tile whose row is known
+      // to be all zero.
       auto qk = [&](int ch, f32x16 (&sc)[KC]) {
 #pragma unroll
         for (int u = 0; u < KC; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            if constexpr (ZI) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sc[u][4 * i + j] = 0.f;
+              continue;
+            }
             const f32x4 bv = *reinterpret_cast<const f32x4*>(
                 bias_lds + 32 * (ch * KC + u) + 8 * i + 4 * hl);
             if constexpr (VN) {
@@ -577,10 +585,28 @@ fwd_bf16_kernel(FwdArgs p) {
         tile(ic<1>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
     }
   } else {
-    for (int t = 0; t < ntiles; t += 2) {
-      tile(ic<0>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
-      if (t + 1 < ntiles)
-        tile(ic<0>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+    // With one key block per tile, a used exact tile's bias row is all zero unless its key
+    // block runs past N (only the last): an even number of the clean tiles first, scores
+    // starting from zero with no bias-row reads, then the rest from their bias rows.
+    if constexpr (G == 1) {
+      int n_clean = n_ex;
+      if (n_ex > 0 && ((sload(p.pcol, e0 + n_ex - 1) >> kEntPartial) & 1)) n_clean -= 1;
+      int t = 0;
+      for (; t < (n_clean & ~1); t += 2) {
+        tile(ic<2>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+        tile(ic<2>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+      }
+      for (; t < ntiles; t += 2) {
+        tile(ic<0>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+        if (t + 1 < ntiles)
+          tile(ic<0>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+      }
+    } else {
+      for (int t = 0; t < ntiles; t += 2) {
+        tile(ic<0>{}, t, k_s0, v_s0, bias_s0, w_s0, k_s1, v_s1, bias_s1, w_s1);
+        if (t + 1 < ntiles)
+          tile(ic<0>{}, t + 1, k_s1, v_s1, bias_s1, w_s1, k_s0, v_s0, bias_s0, w_s0);
+      }
     }
   }
 
