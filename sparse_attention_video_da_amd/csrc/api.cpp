@@ -48,6 +48,7 @@ struct da_plan_s {
   int32_t* d_part = nullptr;
   int32_t* d_psq = nullptr;
   int64_t bytes = 0;
+  int32_t ncu = 0;   // compute units of the plan's device
   int device = 0;
 };
 
@@ -190,7 +191,10 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
     delete p;
     return DA_ERR_DEVICE;
   }
-  if (prepare_device(p->device) != hipSuccess) {
+  if (prepare_device(p->device) != hipSuccess ||
+      hipDeviceGetAttribute(&p->ncu, hipDeviceAttributeMultiprocessorCount, p->device) !=
+          hipSuccess ||
+      p->ncu < 1) {
     (void)hipGetLastError();
     delete p;
     return DA_ERR_DEVICE;
@@ -323,6 +327,7 @@ da_status reassign_impl(da_plan p, const void* K, const void* V, const void* cen
   a.block = d.block;
   a.mask_heads = d.mask_heads;
   a.kblock = p->kblock;
+  a.ncu = p->ncu;
   const hipError_t e = da::launch_reassign(a, d.head_dim, d.dtype == DA_DTYPE_BF16,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ERR_DEVICE;

@@ -55,6 +55,7 @@ struct ReassignArgs {
   float* kvar;     // [H][C] key variance output, or null (not computed)
   int H, N, C, nb, block, mask_heads;
   int kblock;      // exact key block size S
+  int ncu;         // compute units of the device (grid of the persistent assignment)
 };
 
 // Return hipSuccess or the first launch error.

@@ -81,74 +81,26 @@ centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | ((n >> 4) << 14); }
 
-// WAVES waves x 64 keys per workgroup (2 key tiles of 32 per wave; 4 waves, two
-// workgroups per CU, by default). Centroid chunks of CH (128 by default) stream into two
-// swizzled LDS buffers by direct buffer loads, each waited for on its own. The score tile
+// One wave's share of the bf16 assignment: 2 key tiles of 32 keys. The score tile
 // D^T = mu * K^T gives each lane one key and 16 centroids per 32-centroid tile; the lane
 // packs a 5-bit tile-local index into the low mantissa bits of each distance (a change
 // below 2^-18 relative, far inside the 1e-4 tie band) and keeps the integer minimum with
 // three-way mins. Distances are non-negative up to rounding; a slightly negative one (a key
 // equal to a centroid) orders below every positive one as an integer, which is the right
 // winner.
-template <int D, int WAVES, int CH>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
-                   const uint16_t* __restrict__ aug, int32_t* __restrict__ assign, int N,
-                   int C) {
+constexpr int kAsgKtw = 2;
+
+// This lane's keys: the B operand of D^T = mu K^T (dims 16s + 8hl .. +7), and the
+// augmented row for |k|^2 on the lower half (zero on the upper half, so whatever the
+// centroid side holds in dims 8..15 of that step contributes nothing). Keys at or past N
+// are zero.
+template <int D>
+__device__ __forceinline__ void assign_load_keys(const uint16_t* Kh, int key0, int N, int hl,
+                                                 bf16x8 (&kreg)[kAsgKtw][D / 16],
+                                                 bf16x8 (&kaug)[kAsgKtw]) {
   constexpr int DS = D / 16;
-  constexpr int NCH = D / 8;
-  constexpr int THREADS = WAVES * 64;
-  constexpr int KTW = 2;
-  constexpr int KEYS = (THREADS / 64) * 32 * KTW;
-  constexpr int PER_T = CH * NCH / THREADS;
-  static_assert(PER_T * THREADS == CH * NCH, "chunk must split evenly");
-  __shared__ __attribute__((aligned(256))) char mu_s0[CH * D * 2];
-  __shared__ __attribute__((aligned(256))) char mu_s1[CH * D * 2];
-  __shared__ __attribute__((aligned(16))) char aug_s0[CH * 16];
-  __shared__ __attribute__((aligned(16))) char aug_s1[CH * 16];
-
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5;
-  const int l32 = lane & 31;
-  const int key0 = blockIdx.x * KEYS + w * (32 * KTW) + l32;
-  const uint16_t* Kh = K + (size_t)h * N * D;
-  const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(mup + (size_t)h * C * D), (short)0, C * D * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(aug + (size_t)h * C * 8), (short)0, C * 16, kBufferWord3);
-  const int nchunks = (C + CH - 1) / CH;
-
-  // Stage chunk ci: rows past the chunk's valid count re-read its last row (their
-  // distances are masked below).
-  auto stage = [&](int ci, char* ms, char* as) {
-    const int c0 = ci * CH;
-    const int valid = min(CH, C - c0);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int slot = i * THREADS + tid;
-      const int row = slot / NCH;
-      const int pc = slot - row * NCH;
-      const int off = (c0 + min(row, valid - 1)) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rM, (__attribute__((address_space(3))) void*)(ms + (i * THREADS + w * 64) * 16), 16,
-          off, 0, 0, 0);
-    }
-    if (tid < CH)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (__attribute__((address_space(3))) void*)(as + w * 64 * 16), 16,
-          (c0 + min(tid, valid - 1)) * 16, 0, 0, 0);
-  };
-
-  // This lane's keys: the B operand of D^T = mu K^T (dims 16s + 8hl .. +7), and the
-  // augmented row for |k|^2 on the lower half (zero on the upper half, so whatever the
-  // centroid side holds in dims 8..15 of that step contributes nothing).
-  bf16x8 kreg[KTW][DS];
-  bf16x8 kaug[KTW];
-#pragma unroll
-  for (int kt = 0; kt < KTW; ++kt) {
+  for (int kt = 0; kt < kAsgKtw; ++kt) {
     const int key = key0 + 32 * kt;
     float part = 0.f;
 #pragma unroll
@@ -169,20 +121,20 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
     const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
     kaug[kt] = hl == 0 ? bf16x8{one, one, one, n0, n1, n2, zero, zero} : bf16x8{};
   }
+}
 
-  // The centroid chunks are staged after the key loads are issued, so waiting for a chunk
-  // (vmcnt counts in issue order) never waits for more than the loads issued after it.
-  stage(0, mu_s0, aug_s0);
-  if (nchunks > 1) stage(1, mu_s1, aug_s1);
-
-  int bestp[KTW], bbase[KTW];
-#pragma unroll
-  for (int kt = 0; kt < KTW; ++kt) {
-    bestp[kt] = 0x7fffffff;
-    bbase[kt] = 0;
-  }
-  // distance tile ct of a staged chunk: D/16 + 1 MFMAs per key tile
-  auto tile_mfma = [&](const char* ms, const char* as, int ct, f32x16 (&acc)[KTW]) {
+// Running packed minimum of this wave's keys over one LDS chunk of centroid operands: rows
+// c0 .. c0 + valid - 1 (valid <= CH), stored as the staging below lays them out.
+template <int D, int CH>
+__device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int c0, int valid,
+                                             int l32, int hl,
+                                             const bf16x8 (&kreg)[kAsgKtw][D / 16],
+                                             const bf16x8 (&kaug)[kAsgKtw],
+                                             int (&bestp)[kAsgKtw], int (&bbase)[kAsgKtw]) {
+  constexpr int DS = D / 16;
+  constexpr int KTW = kAsgKtw;
+  // distance tile ct of the chunk: D/16 + 1 MFMAs per key tile
+  auto tile_mfma = [&](int ct, f32x16 (&acc)[KTW]) {
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) acc[kt] = f32x16{};
 #pragma unroll
@@ -218,56 +170,148 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
     }
   };
   constexpr int NT = CH / 32;
-  auto compute = [&](int ci, const char* ms, const char* as) {
-    const int c0 = ci * CH;
-    const int valid = min(CH, C - c0);
-    if (valid == CH) {
-      // full chunk, software-pipelined: the MFMAs of tile t+1 run beside the argmin of t,
-      // and the centroid operands of tile t+2 are read meanwhile into the register set
-      // tile t has just released
-      f32x16 acc[2][KTW];
-      bf16x8 ops[2][DS + 1];
-      auto load_ops = [&](int ct, bf16x8 (&o)[DS + 1]) {
+  if (valid == CH) {
+    // full chunk, software-pipelined: the MFMAs of tile t+1 run beside the argmin of t,
+    // and the centroid operands of tile t+2 are read meanwhile into the register set
+    // tile t has just released
+    f32x16 acc[2][KTW];
+    bf16x8 ops[2][DS + 1];
+    auto load_ops = [&](int ct, bf16x8 (&o)[DS + 1]) {
 #pragma unroll
-        for (int s = 0; s < DS; ++s) o[s] = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
-        o[DS] = lds_read_b128(as, (32 * ct + l32) * 16);
-      };
-      auto mfma_ops = [&](const bf16x8 (&o)[DS + 1], f32x16 (&acc_)[KTW]) {
+      for (int s = 0; s < DS; ++s) o[s] = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
+      o[DS] = lds_read_b128(as, (32 * ct + l32) * 16);
+    };
+    auto mfma_ops = [&](const bf16x8 (&o)[DS + 1], f32x16 (&acc_)[KTW]) {
 #pragma unroll
-        for (int kt = 0; kt < KTW; ++kt) acc_[kt] = f32x16{};
+      for (int kt = 0; kt < KTW; ++kt) acc_[kt] = f32x16{};
 #pragma unroll
-        for (int s = 0; s <= DS; ++s)
+      for (int s = 0; s <= DS; ++s)
 #pragma unroll
-          for (int kt = 0; kt < KTW; ++kt)
-            acc_[kt] = mfma32x32x16(o[s], s < DS ? kreg[kt][s] : kaug[kt], acc_[kt]);
-      };
-      load_ops(0, ops[0]);
-      if (NT > 1) load_ops(1, ops[1]);
-      mfma_ops(ops[0], acc[0]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int kt = 0; kt < KTW; ++kt)
+          acc_[kt] = mfma32x32x16(o[s], s < DS ? kreg[kt][s] : kaug[kt], acc_[kt]);
+    };
+    load_ops(0, ops[0]);
+    if (NT > 1) load_ops(1, ops[1]);
+    mfma_ops(ops[0], acc[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t + 1 < NT) mfma_ops(ops[(t + 1) & 1], acc[(t + 1) & 1]);
-        if (t + 2 < NT) load_ops(t + 2, ops[t & 1]);
-        tile_min(acc[t & 1], c0 + 32 * t, false, 0);
-        if (t + 1 < NT) {
+    for (int t = 0; t < NT; ++t) {
+      if (t + 1 < NT) mfma_ops(ops[(t + 1) & 1], acc[(t + 1) & 1]);
+      if (t + 2 < NT) load_ops(t + 2, ops[t & 1]);
+      tile_min(acc[t & 1], c0 + 32 * t, false, 0);
+      if (t + 1 < NT) {
 #pragma unroll
-          for (int g = 0; g < DS + 1; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, KTW, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-          }
+        for (int g = 0; g < DS + 1; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, KTW, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      const int ntile = (valid + 31) / 32;
-      for (int ct = 0; ct < ntile; ++ct) {
-        f32x16 acc[KTW];
-        tile_mfma(ms, as, ct, acc);
-        tile_min(acc, c0 + 32 * ct, 32 * ct + 32 > valid, c0 + valid);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  } else {
+    const int ntile = (valid + 31) / 32;
+    for (int ct = 0; ct < ntile; ++ct) {
+      f32x16 acc[KTW];
+      tile_mfma(ct, acc);
+      tile_min(acc, c0 + 32 * ct, 32 * ct + 32 > valid, c0 + valid);
+    }
+  }
+}
+
+// Merge the two half-waves' minima of each key (ties to the lower centroid) and store.
+__device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
+                                             const int (&bbase)[kAsgKtw], int hl, int key0,
+                                             int N, int32_t* __restrict__ assign_h) {
+#pragma unroll
+  for (int kt = 0; kt < kAsgKtw; ++kt) {
+    const int mv = bestp[kt] & ~0x1f;
+    const int mc = bbase[kt] + (bestp[kt] & 0x1f) + 4 * hl;
+    const int ov = __shfl_xor(mv, 32, 64);
+    const int oc = __shfl_xor(mc, 32, 64);
+    const int bi = (ov < mv || (ov == mv && oc < mc)) ? oc : mc;
+    const int key = key0 + 32 * kt;
+    if (hl == 0 && key < N) assign_h[key] = bi;
+  }
+}
+
+// Stage centroid rows c0 .. c0 + CH - 1 of one head (rows past C re-read row C - 1; their
+// distances are masked) into an LDS chunk: the -2 mu operands swizzled by row, and the
+// augmented rows, by direct buffer loads. The threads of the workgroup share the work.
+template <int D, int CH, int THREADS>
+__device__ __forceinline__ void assign_stage(__amdgpu_buffer_rsrc_t rM, __amdgpu_buffer_rsrc_t rA,
+                                             int c0, int C, int tid, int w, char* ms, char* as) {
+  constexpr int NCH = D / 8;
+  constexpr int PER_T = CH * NCH / THREADS;
+  static_assert(PER_T * THREADS == CH * NCH, "chunk must split evenly");
+  const int valid = min(CH, C - c0);
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int slot = i * THREADS + tid;
+    const int row = slot / NCH;
+    const int pc = slot - row * NCH;
+    const int off = (c0 + min(row, valid - 1)) * (D * 2) + ((pc ^ swz_key<D>(row)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rM, (__attribute__((address_space(3))) void*)(ms + (i * THREADS + w * 64) * 16), 16,
+        off, 0, 0, 0);
+  }
+  static_assert(CH % 64 == 0 && CH <= THREADS, "augmented rows: one load per thread");
+  if (tid < CH)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rA, (__attribute__((address_space(3))) void*)(as + w * 64 * 16), 16,
+        (c0 + min(tid, valid - 1)) * 16, 0, 0, 0);
+}
+
+// Streaming form, any C: WAVES waves x 64 keys per workgroup (4 waves, two workgroups per
+// CU, by default). Centroid chunks of CH (128 by default) stream into two swizzled LDS
+// buffers by direct buffer loads, each waited for on its own.
+template <int D, int WAVES, int CH>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
+                   const uint16_t* __restrict__ aug, int32_t* __restrict__ assign, int N,
+                   int C) {
+  constexpr int DS = D / 16;
+  constexpr int NCH = D / 8;
+  constexpr int THREADS = WAVES * 64;
+  constexpr int KTW = kAsgKtw;
+  constexpr int KEYS = (THREADS / 64) * 32 * KTW;
+  constexpr int PER_T = CH * NCH / THREADS;
+  __shared__ __attribute__((aligned(256))) char mu_s0[CH * D * 2];
+  __shared__ __attribute__((aligned(256))) char mu_s1[CH * D * 2];
+  __shared__ __attribute__((aligned(16))) char aug_s0[CH * 16];
+  __shared__ __attribute__((aligned(16))) char aug_s1[CH * 16];
+
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+  const int key0 = blockIdx.x * KEYS + w * (32 * KTW) + l32;
+  const uint16_t* Kh = K + (size_t)h * N * D;
+  const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(mup + (size_t)h * C * D), (short)0, C * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(aug + (size_t)h * C * 8), (short)0, C * 16, kBufferWord3);
+  const int nchunks = (C + CH - 1) / CH;
+
+  bf16x8 kreg[KTW][DS];
+  bf16x8 kaug[KTW];
+  assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug);
+
+  // The centroid chunks are staged after the key loads are issued, so waiting for a chunk
+  // (vmcnt counts in issue order) never waits for more than the loads issued after it.
+  assign_stage<D, CH, THREADS>(rM, rA, 0, C, tid, w, mu_s0, aug_s0);
+  if (nchunks > 1) assign_stage<D, CH, THREADS>(rM, rA, CH, C, tid, w, mu_s1, aug_s1);
+
+  int bestp[KTW], bbase[KTW];
+#pragma unroll
+  for (int kt = 0; kt < KTW; ++kt) {
+    bestp[kt] = 0x7fffffff;
+    bbase[kt] = 0;
+  }
+  auto compute = [&](int ci, const char* ms, const char* as) {
+    assign_chunk<D, CH>(ms, as, ci * CH, min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase);
   };
   // Chunk ci sits in buffer ci % 2. Before computing it, each thread waits only until its
   // loads of chunk ci are done (the next chunk's may still be in flight), then the
@@ -286,25 +330,82 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
     compute(ci, mu_s0, aug_s0);
     if (ci + 1 < nchunks) {
       __builtin_amdgcn_s_barrier();   // every wave is done with buffer 0
-      if (ci + 2 < nchunks) stage(ci + 2, mu_s0, aug_s0);
+      if (ci + 2 < nchunks) assign_stage<D, CH, THREADS>(rM, rA, (ci + 2) * CH, C, tid, w, mu_s0, aug_s0);
       wait_chunk(ci + 2 < nchunks);
       compute(ci + 1, mu_s1, aug_s1);
       if (ci + 3 < nchunks) {
         __builtin_amdgcn_s_barrier();   // every wave is done with buffer 1
-        stage(ci + 3, mu_s1, aug_s1);
+        assign_stage<D, CH, THREADS>(rM, rA, (ci + 3) * CH, C, tid, w, mu_s1, aug_s1);
       }
     }
   }
+  assign_store(bestp, bbase, hl, key0, N, assign + (size_t)h * N);
+}
 
+// Resident form, C <= kAsgResidentRows(D): the whole table of one head stays in LDS (128 KB
+// of operands plus the augmented rows) and the keys stream past it. One workgroup of WAVES
+// waves per CU, a persistent grid: workgroup g takes units [g U / G, (g+1) U / G) of the
+// U = H * ceil(N / 64) units of 64 keys in (head, key) order, reloading the table where its
+// range enters the next head; between reloads every wave walks its own units (u = first +
+// w, + WAVES, ...) with no barrier, so one wave's key loads hide behind the others' MFMAs.
+template <int D>
+constexpr int kAsgResidentRows = 65536 / D;   // 128 KB of bf16 operands
+template <int D, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
+                            const uint16_t* __restrict__ aug, int32_t* __restrict__ assign,
+                            int H, int N, int C) {
+  constexpr int DS = D / 16;
+  constexpr int CH = 128;
+  constexpr int ROWS = kAsgResidentRows<D>;
+  constexpr int THREADS = WAVES * 64;
+  constexpr int KTW = kAsgKtw;
+  static_assert(ROWS % CH == 0, "whole chunks");
+  __shared__ __attribute__((aligned(256))) char mu_s[ROWS * D * 2];
+  __shared__ __attribute__((aligned(16))) char aug_s[ROWS * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+  const int nchunks = (C + CH - 1) / CH;
+  const int upn = (N + 63) / 64;   // units per head
+  const long long U = (long long)H * upn;
+  const int G = gridDim.x;
+  int u = (int)(U * blockIdx.x / G);
+  const int u_end = (int)(U * (blockIdx.x + 1) / G);
+  while (u < u_end) {
+    const int h = u / upn;
+    const int seg_end = min(u_end, (h + 1) * upn);
+    const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(mup + (size_t)h * C * D), (short)0, C * D * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(aug + (size_t)h * C * 8), (short)0, C * 16, kBufferWord3);
+    __builtin_amdgcn_s_barrier();   // every wave is done with the previous head's table
+    for (int ci = 0; ci < nchunks; ++ci)
+      assign_stage<D, CH, THREADS>(rM, rA, ci * CH, C, tid, w, mu_s + ci * CH * D * 2,
+                                   aug_s + ci * CH * 16);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    const uint16_t* Kh = K + (size_t)h * N * D;
+    for (int v = u + w; v < seg_end; v += WAVES) {
+      const int key0 = (v - h * upn) * 64 + l32;
+      bf16x8 kreg[KTW][DS];
+      bf16x8 kaug[KTW];
+      assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug);
+      int bestp[KTW], bbase[KTW];
 #pragma unroll
-  for (int kt = 0; kt < KTW; ++kt) {
-    const int mv = bestp[kt] & ~0x1f;
-    const int mc = bbase[kt] + (bestp[kt] & 0x1f) + 4 * hl;
-    const int ov = __shfl_xor(mv, 32, 64);
-    const int oc = __shfl_xor(mc, 32, 64);
-    const int bi = (ov < mv || (ov == mv && oc < mc)) ? oc : mc;
-    const int key = key0 + 32 * kt;
-    if (hl == 0 && key < N) assign[(size_t)h * N + key] = bi;
+      for (int kt = 0; kt < KTW; ++kt) {
+        bestp[kt] = 0x7fffffff;
+        bbase[kt] = 0;
+      }
+      for (int ci = 0; ci < nchunks; ++ci)
+        assign_chunk<D, CH>(mu_s + ci * CH * D * 2, aug_s + ci * CH * 16, ci * CH,
+                            min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase);
+      assign_store(bestp, bbase, hl, key0, N, assign + (size_t)h * N);
+    }
+    u = seg_end;
   }
 }
 
@@ -754,10 +855,15 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
     uint16_t* aug = a.cop + (size_t)a.H * a.C * D;
     hipLaunchKernelGGL((centroid_operands_kernel<D>), dim3((a.C + 255) / 256, a.H), dim3(256), 0,
                        s, static_cast<const uint16_t*>(a.mu_in), mup, aug, a.C);
-    constexpr int AW = ASG_WAVES;
-    hipLaunchKernelGGL((assign_bf16_kernel<D, AW, ASG_CH>), dim3((a.N + AW * 64 - 1) / (AW * 64), a.H),
-                       dim3(AW * 64), 0, s, static_cast<const uint16_t*>(a.K), mup, aug, a.assign,
-                       a.N, a.C);
+    if (a.C <= kAsgResidentRows<D>) {
+      hipLaunchKernelGGL((assign_resident_bf16_kernel<D, 8>), dim3(a.ncu), dim3(8 * 64), 0, s,
+                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, a.H, a.N, a.C);
+    } else {
+      constexpr int AW = ASG_WAVES;
+      hipLaunchKernelGGL((assign_bf16_kernel<D, AW, ASG_CH>),
+                         dim3((a.N + AW * 64 - 1) / (AW * 64), a.H), dim3(AW * 64), 0, s,
+                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, a.N, a.C);
+    }
   }
   else
     hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,

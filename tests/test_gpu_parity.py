@@ -186,13 +186,17 @@ def test_ragged_shapes(lib, d, B, dtype, N):
               f"ragged d{d} B{B} {dtype}")
 
 
-@pytest.mark.parametrize("N,C", [(900, 20), (2000, 300), (4000, 2048)])
-def test_cluster_count_edges(lib, N, C):
+@pytest.mark.parametrize("N,C,d", [(900, 20, 128), (2000, 300, 128), (4000, 2048, 128),
+                                   (3000, 512, 128), (3000, 513, 128), (5000, 1024, 64),
+                                   (5000, 1025, 64)])
+def test_cluster_count_edges(lib, N, C, d):
     """bf16 cluster counts away from the tile sizes: fewer centroids than one 32-wide
     distance tile (C = 20), an odd number of 128-centroid staging chunks with a ragged last
     one (C = 300: 3 chunks), and many chunks with mostly tiny or empty clusters
-    (C = 2048: 16 chunks, about 2 keys per cluster, many refresh segments)."""
-    H, d, B = 2, 128, 128
+    (C = 2048: 16 chunks, about 2 keys per cluster, many refresh segments); and both sides of
+    the largest table the assignment keeps resident in LDS (128 KB of operands: C = 512 at
+    d = 128, 1024 at d = 64), past which it streams the table in chunks."""
+    H, B = 2, 128
     L, cache = _random_layer(300 + C, H, N, d, "bf16", C, G=max(2, C // 4))
     nb = -(-N // B)
     rng = np.random.default_rng(C)
