@@ -4,9 +4,11 @@
 //
 // Kernel sequence per call (one stream, no host synchronisation):
 //   0. operands      (bf16) per centroid: -2 mu and the split |mu|^2 row for the MFMA.
-//   1. assign        MFMA distance product against LDS-staged centroid chunks, per-lane
-//                    running argmin, written as int32 (bf16: any centroid within the
-//                    1e-4 relative tie band of the nearest; fp32: lowest index on ties).
+//   1. assign        MFMA distance product against centroid operands in LDS (bf16: the
+//                    whole table of a head resident when it fits in 128 KB, with a
+//                    persistent grid; streamed in chunks otherwise), per-lane running
+//                    argmin, written as int32 (bf16: any centroid within the 1e-4 relative
+//                    tie band of the nearest; fp32: lowest index on ties).
 //   2. block_hist    per key block, an LDS-atomic histogram of its keys' clusters.
 //   3. col_scan      per cluster, exclusive prefix of the histograms over key blocks
 //                    (where each block's keys start inside the cluster) and the sizes.
@@ -342,8 +344,9 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
   assign_store(bestp, bbase, hl, key0, N, assign + (size_t)h * N);
 }
 
-// Resident form, C <= kAsgResidentRows(D): the whole table of one head stays in LDS (128 KB
-// of operands plus the augmented rows) and the keys stream past it. One workgroup of WAVES
+// Resident form, C <= kAsgResidentRows<D> (512 at d = 128, 1024 at d = 64): the whole table
+// of one head stays in LDS (128 KB of operands plus the augmented rows) and the keys stream
+// past it. One workgroup of WAVES
 // waves per CU, a persistent grid: workgroup g takes units [g U / G, (g+1) U / G) of the
 // U = H * ceil(N / 64) units of 64 keys in (head, key) order, reloading the table where its
 // range enters the next head; between reloads every wave walks its own units (u = first +
