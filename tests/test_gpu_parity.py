@@ -205,6 +205,25 @@ def test_cluster_count_edges(lib, N, C, d):
               f"clusters C={C} N={N}")
 
 
+@pytest.mark.parametrize("H,N,C", [(1, 200, 16), (7, 37000, 64)])
+def test_assignment_work_split(lib, H, N, C):
+    """The resident assignment splits H * ceil(N / 64) units of 64 keys over one workgroup
+    per CU: far fewer units than workgroups (4 units, a ragged last one, most workgroups
+    empty), and many units per workgroup with head boundaries inside workgroup ranges
+    (7 heads of 579 units: about 16 units a workgroup on 256 CUs), where a workgroup reloads
+    the centroid table of the next head. Every head's assignments, sizes, counts and cache
+    against the oracle; the forward on a sparse mask (2 exact blocks per query block)."""
+    d, B = 128, 128
+    L, cache = _random_layer(1500 + H, H, N, d, "bf16", C, G=max(2, C // 4))
+    nb = -(-N // B)
+    rng = np.random.default_rng(H)
+    mask = np.zeros((1, nb, nb), np.uint8)
+    for b in range(nb):
+        mask[0, b, rng.choice(nb, size=min(2, nb), replace=False)] = 1
+    _run_case(lib, L, cache, mask, dict(H=H, N=N, d=d, B=B, C=C, dtype="bf16"),
+              f"assignment work split H={H} N={N}")
+
+
 # ----------------------------------------------------------------- key blocks smaller than B
 @pytest.mark.parametrize("name", ["small_sub32_bf16", "small_sub16_d64_bf16", "tiny_sub_f32"])
 def test_key_block_configs(lib, name):
