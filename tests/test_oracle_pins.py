@@ -445,6 +445,62 @@ def test_zero_variance_is_the_plain_forward():
                        kvar=np.zeros(st["mu1"].shape[0]))
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
-    # a cluster holding one key has no spread
-    single = np.nonzero(st["sizes"] == 1)[0]
-    assert np.all(st["kvar"][single] == 0) and np.all(st["kvar"] >= 0)
+    assert np.all(st["kvar"] >= 0)
+
+
+# ----------------------------------------------------------------- tie band and key variance
+def _frac(x):
+    from fractions import Fraction
+    if isinstance(x, list):
+        return Fraction(int(x[0]), int(x[1]))
+    return Fraction(x)
+
+
+def test_near_tie_gaps_are_the_hand_derived_fractions():
+    """Relative top-two gaps (D2 - D1) / D2 of hand-placed near ties (about 6e-5, 2.4e-4, just
+    under 1e-4, 9e-5): exact fractions, so a gap measured against D1, a dropped square or a
+    swapped pair changes them."""
+    g = json.load(open(os.path.join(GOLDEN, "near_ties_and_key_variance.json")))["near_ties"]
+    e = g["expected"]
+    K = np.array(g["keys"], float)[:, None]
+    mu = np.array([float(_frac(c)) for c in g["centroids"]])[:, None]
+    a, gap, d1, d2 = O.assign(K, mu)
+    assert a.tolist() == e["assign"]
+    assert d1.tolist() == [float(e["d1"])] * len(K)
+    np.testing.assert_allclose(d2, [float(_frac(x)) for x in e["d2"]], rtol=1e-15)
+    np.testing.assert_allclose(gap, [float(_frac(x)) for x in e["gap"]], rtol=1e-12)
+    # the parity rule excuses a mismatch only inside the band
+    assert (gap < O.TIE_BAND).tolist() == e["inside_band"]
+
+
+def test_tie_band_membership_is_measured_against_the_candidate_distance():
+    """assignment_allowed accepts a centroid whose squared distance exceeds the minimum by
+    0.90e-4 of itself and by 0.99994e-4 of itself (more than 1e-4 of the minimum: a band
+    measured against D1 would reject it), and rejects ones at 1.10e-4 and 2.4e-4."""
+    g = json.load(open(os.path.join(GOLDEN, "near_ties_and_key_variance.json")))["near_ties"]
+    K = np.array(g["keys"], float)[:, None]
+    mu = np.array([float(_frac(c)) for c in g["centroids"]])[:, None]
+    _, _, d1, _ = O.assign(K, mu)
+    for key, c, want in g["expected"]["allowed_tests"]:
+        got = O.assignment_allowed(K[key:key + 1], mu, np.array([c]), d1[key:key + 1])
+        assert bool(got[0]) is want, (key, c)
+    # the minimum itself is always allowed
+    assert O.assignment_allowed(K, mu, np.array(g["expected"]["assign"]), d1).all()
+
+
+def test_key_variance_is_centred_on_the_new_mean():
+    """kvar of a cluster whose mean (2, 2/3) is not its cached centroid (2, 1): 7/9 around the
+    mean (5/6 around the cached centroid would be wrong); a single-key cluster and an empty
+    one have zero variance, and the empty one keeps its cached centroid."""
+    from fractions import Fraction
+    g = json.load(open(os.path.join(GOLDEN, "near_ties_and_key_variance.json")))["variance"]
+    e = g["expected"]
+    K = np.array(g["keys"], float)
+    mu0 = np.array(g["mu0"], float)
+    st = O.reassign_step(K, np.zeros_like(K), mu0, np.zeros((1, 1), np.uint8), 4, "f64")
+    assert st["assign"].tolist() == e["assign"]
+    assert st["sizes"].tolist() == e["sizes"]
+    want_mu = np.array([[float(Fraction(x)) for x in row] for row in e["mu1"]])
+    np.testing.assert_allclose(st["mu1_exact"], want_mu, rtol=1e-15)
+    np.testing.assert_allclose(st["kvar"], [float(Fraction(x)) for x in e["kvar"]], rtol=1e-14,
+                               atol=0)
