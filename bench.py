@@ -80,6 +80,25 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, L, mask, budget_s: float):
     """The fp64 oracle on a bounded sample of the same workload, extrapolated to ms/layer."""
     import oracle as O
@@ -119,7 +138,7 @@ def cpu_baseline(cfg, L, mask, budget_s: float):
     per_head_s = t_assign + t_refresh + t_fwd * nb / max(done, 1)
     ms_layer = per_head_s * cfg.heads * 1e3
     out = {"value": round(ms_layer, 1), "unit": "ms/layer", "cores": int(cores),
-           "kind": "oracle",
+           "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
            "sample": (f"head 0 of {cfg.heads}: assignment of {nk} of {cfg.seq_len} keys, "
                       f"refresh+counts over all keys, forward of {done} of {nb} query blocks "
                       f"(fp64 numpy); extrapolated linearly to all blocks and heads")}

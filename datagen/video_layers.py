@@ -8,18 +8,16 @@ uniformly, and K_t = centre + sigma * N(0, I), Q_t likewise with its own compone
 noise draws (K and Q share the head's centres); V ~ N(0, I). Values are produced in
 float32 and stored in the layer's dtype (bf16 by round-to-nearest-even, or float32).
 
-Optional positional locality (`locality` a > 0, off in every named workload): Q_t and K_t
-both gain a * phi(x_t), where x_t = (S*f, r, w) are the token's scaled 3D coordinates (S
-as in the local masks) and phi are d random Fourier features of x with frequencies
-N(0, I / l^2) and uniform phases, scaled so |phi| is about 1. Then phi(x).phi(y) is about
-exp(-|x - y|^2 / (2 l^2)), so every logit gains about scale * a^2 times a Gaussian of the
-query-key distance: attention that decays with 3D distance, the structure that makes
-position-fixed exact blocks worth keeping.
+Optional shared offset (`key_offset` s, 0 in every named workload): every mixture centre
+gains s in every dimension, so Q and K sit far from the origin (|k|^2 about d (1 + s^2))
+while their spread stays sigma. It draws nothing, so the offset layer's noise is the plain
+layer's; it exercises distance arithmetic whose rounding grows with |k|^2 rather than with
+the distances themselves.
 
 Every random stream is seeded with numpy's SeedSequence over the tuple
 (config id, head, stream, step), so any single head can be regenerated on its own.
 Streams: 0 centres, 1 K components, 2 K noise, 3 Q components, 4 Q noise, 5 V,
-6 K drift, 7 V drift, 8 mask, 9 cache seed, 10 positional features.
+6 K drift, 7 V drift, 8 mask, 9 cache seed.
 
 The mask is a plan input: position-fixed exact key blocks per query block. Three kinds:
   * "random": the diagonal block plus (k - 1) distinct seeded other blocks per row;
@@ -51,7 +49,6 @@ import numpy as np
 
 STREAM_CENTRES, STREAM_KCOMP, STREAM_KNOISE, STREAM_QCOMP, STREAM_QNOISE = 0, 1, 2, 3, 4
 STREAM_V, STREAM_KDRIFT, STREAM_VDRIFT, STREAM_MASK, STREAM_CACHE = 5, 6, 7, 8, 9
-STREAM_POS = 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -77,8 +74,7 @@ class LayerConfig:
     drift_sigma: float = 0.05
     description: str = ""
     key_block: int = 0      # exact key block size (0: the query block size)
-    locality: float = 0.0   # amplitude a of the positional term of Q and K (0: none)
-    locality_len: float = 6.0   # its length scale l, in scaled 3D token coordinates
+    key_offset: float = 0.0     # added to every coordinate of every mixture centre
     local_rule: str = "centre"  # key block distance for "local" masks: "centre" | "reach"
 
     @property
@@ -240,28 +236,15 @@ def head_tensors(cfg: LayerConfig, head: int) -> Dict[str, np.ndarray]:
     n, d, g = cfg.seq_len, cfg.head_dim, cfg.mixture
     sig = np.float32(cfg.sigma)
     centres = _rng(cfg, head, STREAM_CENTRES).standard_normal((g, d), dtype=np.float32)
+    if cfg.key_offset:
+        centres += np.float32(cfg.key_offset)
     kc = _rng(cfg, head, STREAM_KCOMP).integers(0, g, size=n)
     k = centres[kc] + sig * _rng(cfg, head, STREAM_KNOISE).standard_normal((n, d), dtype=np.float32)
     qc = _rng(cfg, head, STREAM_QCOMP).integers(0, g, size=n)
     q = centres[qc] + sig * _rng(cfg, head, STREAM_QNOISE).standard_normal((n, d), dtype=np.float32)
     v = _rng(cfg, head, STREAM_V).standard_normal((n, d), dtype=np.float32)
-    if cfg.locality > 0:
-        pos = np.float32(cfg.locality) * _positional_features(cfg, head)
-        q += pos
-        k += pos
     return {"Q": _store(cfg, q), "K": _store(cfg, k), "V": _store(cfg, v),
             "k_component": kc.astype(np.int64)}
-
-
-def _positional_features(cfg: LayerConfig, head: int) -> np.ndarray:
-    """[N][d] float32 random Fourier features of the scaled 3D token coordinates."""
-    n, d, hw, w = cfg.seq_len, cfg.head_dim, cfg.height * cfg.width, cfg.width
-    t = np.arange(n, dtype=np.int64)
-    x = np.stack([cfg.local_scale * (t // hw), (t // w) % cfg.height, t % w], axis=1)
-    rng = _rng(cfg, head, STREAM_POS)
-    omega = rng.standard_normal((3, d)) / cfg.locality_len
-    phase = rng.uniform(0.0, 2.0 * math.pi, size=d)
-    return (math.sqrt(2.0 / d) * np.cos(x.astype(np.float64) @ omega + phase)).astype(np.float32)
 
 
 def drift_noise(cfg: LayerConfig, head: int, step: int, which: str) -> np.ndarray:

@@ -43,7 +43,7 @@ class DAError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m sparse_attention_video_da_amd.build`"
+            f"{LIB_PATH} is missing: build it with `python sparse_attention_video_da_amd/build.py`"
             " (there is no non-HIP fallback)")
     # PyTorch ships its own HIP runtime under the same soname as the system one this library
     # links. Loading PyTorch first makes the library bind to that one runtime, so the device

@@ -3,7 +3,7 @@
 Compiles every source under csrc/ for gfx950 with hipcc and links one shared library
 exporting only the C ABI declared in include/decoupattn.h.
 
-    python -m sparse_attention_video_da_amd.build [--jobs N]
+    python sparse_attention_video_da_amd/build.py [--jobs N]
 """
 from __future__ import annotations
 

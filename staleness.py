@@ -13,8 +13,7 @@ both caches the step reports
 Dense attention is the library's own forward on a plan whose mask keeps every block exact.
 Everything runs through the C ABI on one GPU; the host only reduces the reported numbers.
 
-    python -m sparse_attention_video_da_amd.staleness [--config extreme_cache_bf16]
-                                                      [--steps 8] [--heads 4]
+    python staleness.py [--config extreme_cache_bf16] [--steps 8] [--heads 4]
 """
 from __future__ import annotations
 
@@ -27,7 +26,7 @@ import time
 
 import numpy as np
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 

@@ -88,28 +88,17 @@ def test_reach_rule_covers_the_query_block_ends():
     assert mean_kernel(rea) > mean_kernel(cen)
 
 
-def test_positional_locality_is_a_distance_kernel_and_off_by_default():
+def test_key_offset_shifts_the_centres_and_draws_nothing():
     import dataclasses
-    from datagen.video_layers import _positional_features, head_tensors
+    from datagen.video_layers import head_tensors, to_f32
     base = get_config("small_bf16")
-    cfg = dataclasses.replace(base, locality=4.0, locality_len=3.0)
-    # phi(x).phi(y) ~ exp(-|x-y|^2 / (2 l^2)) along a row (unit steps), down a column and
-    # across frames. For one head the d frequencies are one Monte Carlo sample of that
-    # kernel (error about sqrt(1/(2d)) = 0.09 at d = 64, whatever the number of token
-    # pairs averaged); averaged over 8 heads with their own frequencies, 4 sigma is 0.13.
-    w = cfg.width
-    phis = [_positional_features(cfg, h).astype(np.float64) for h in range(8)]
-    assert np.allclose(np.mean([np.linalg.norm(p, axis=1).mean() for p in phis]), 1.0,
-                       atol=0.03)
-    for step, dist in ((1, 1.0), (3, 3.0), (w, 1.0), (cfg.height * w, cfg.local_scale)):
-        i = np.arange(0, cfg.seq_len - step, 97)
-        got = float(np.mean([(p[i] * p[i + step]).sum(axis=1).mean() for p in phis]))
-        assert abs(got - np.exp(-dist * dist / (2 * 9.0))) < 0.13, (step, got)
-    # locality 0 draws nothing and leaves the tensors bit-identical
-    a, b = head_tensors(base, 1), head_tensors(dataclasses.replace(base, locality=0.0), 1)
-    assert all((a[k] == b[k]).all() for k in ("Q", "K", "V"))
-    c = head_tensors(cfg, 1)
-    assert (c["V"] == a["V"]).all() and not (c["K"] == a["K"]).all()
+    a = head_tensors(base, 1)
+    b = head_tensors(dataclasses.replace(base, key_offset=3.0), 1)
+    assert (a["V"] == b["V"]).all() and (a["k_component"] == b["k_component"]).all()
+    ka, kb = to_f32(base, a["K"]), to_f32(base, b["K"])
+    # the same noise, shifted by 3 in every coordinate (up to the bf16 rounding of both)
+    assert np.abs((kb - ka) - 3.0).max() <= 2 ** -8 * (np.abs(kb).max() + np.abs(ka).max())
+    assert abs(float(kb.mean()) - float(ka.mean()) - 3.0) < 1e-2
 
 
 def test_generator_is_deterministic_and_per_head():
