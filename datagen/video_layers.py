@@ -191,6 +191,27 @@ CONFIGS: Dict[str, LayerConfig] = {
         mixture=256, sigma=0.25, dtype="bf16", steps=4, drift_k=True, drift_v=True,
         description="40 heads, N=75600, d=128, C=512, 1% 3D-local mask, 4 steps of K,V "
                     "drift with reassign + forward"),
+    "offset_keys_bf16": LayerConfig(
+        "offset_keys_bf16", 14, heads=4, frames=8, height=32, width=32, head_dim=128,
+        block=128, clusters=512, mask_kind="local", blocks_per_row=12, first_frame=False,
+        mixture=256, sigma=0.05, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_offset=3.0,
+        description="4 heads, N=8192 (8x32x32), d=128, C=512: tight clusters (spread 0.05) "
+                    "around centres shifted by 3 in every coordinate, so |k|^2 is about "
+                    "1300 against nearest squared distances about 0.6"),
+    "offset_keys_wide_bf16": LayerConfig(
+        "offset_keys_wide_bf16", 15, heads=2, frames=8, height=32, width=32, head_dim=128,
+        block=128, clusters=1024, mask_kind="local", blocks_per_row=12, first_frame=False,
+        mixture=512, sigma=0.02, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_offset=8.0,
+        description="2 heads, N=8192, d=128, C=1024 (more centroids than fit in LDS at "
+                    "once): spread 0.02 around centres shifted by 8 (|k|^2 about 8300)"),
+    "offset_keys_d64_bf16": LayerConfig(
+        "offset_keys_d64_bf16", 16, heads=3, frames=4, height=32, width=32, head_dim=64,
+        block=64, clusters=256, mask_kind="local", blocks_per_row=16, first_frame=False,
+        mixture=128, sigma=0.03, dtype="bf16", steps=0, drift_k=False, drift_v=False,
+        key_offset=4.0,
+        description="3 heads, N=4096, d=64, C=256: spread 0.03 around centres shifted by 4"),
 }
 
 def get_config(name: str) -> LayerConfig:

@@ -118,7 +118,15 @@ DA_API da_status da_plan_destroy(da_plan plan);
  *                      cluster, rounded to the dtype; a cluster with no key keeps mu0.
  *   mean_values_out    [H][C][d] mean of the values of each cluster's keys (0 if none).
  *   assign_out         [H][N] a_j = argmin_c ||k_j - mu0_c||^2 (squared Euclidean on the
- *                      stored values, fp32 accumulation; exact ties go to the lowest c).
+ *                      stored values). fp32 plans: differences squared and summed in fp32,
+ *                      equal sums go to the lowest c. bf16 plans: distances from the bf16
+ *                      matrix cores with fp32 accumulation; a key whose two nearest
+ *                      centroids are too close for that arithmetic to order (within a bound
+ *                      proportional to 2^-17 (|k|^2 + max |mu|^2)) is re-measured as an fp32
+ *                      sum of squared differences against every centroid, equal sums going
+ *                      to the lowest c. Either way the chosen centroid is the nearest unless
+ *                      the two nearest lie within a relative 1e-4 of each other (then any of
+ *                      them may be chosen).
  *   cluster_sizes_out  [H][C] number of keys per cluster.
  *   qblock_counts_out  [H][nb][C] n[b][c]: keys of cluster c outside query block b's
  *                      exact key blocks (counted key by key, whatever the key block size).

@@ -47,6 +47,7 @@ struct da_plan_s {
   int32_t* d_cop = nullptr;
   int32_t* d_part = nullptr;
   int32_t* d_psq = nullptr;
+  int32_t* d_fix = nullptr;   // near-tie list of the bf16 assignment
   int64_t bytes = 0;
   int32_t ncu = 0;   // compute units of the plan's device
   int device = 0;
@@ -87,7 +88,7 @@ da_status check_desc(const da_desc* d) {
   const int64_t nkb = (d->seq_len + S - 1) / S;
   const int64_t es = d->dtype == DA_DTYPE_BF16 ? 2 : 4;
   if ((int64_t)d->seq_len * d->head_dim * es > INT32_MAX || nb * d->clusters > INT32_MAX ||
-      nb * nkb * d->mask_heads > INT32_MAX)
+      nb * nkb * d->mask_heads > INT32_MAX || (int64_t)d->heads * d->seq_len > INT32_MAX)
     return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
@@ -95,11 +96,12 @@ da_status check_desc(const da_desc* d) {
 void destroy_device(da_plan_s* p) {
   int32_t* bufs[] = {p->d_rowptr, p->d_col,   p->d_prowptr, p->d_pcol,
                      p->d_hist,   p->d_off,   p->d_start,   p->d_perm, p->d_cop,
-                     p->d_part,   p->d_psq};
+                     p->d_part,   p->d_psq,   p->d_fix};
   for (int32_t* b : bufs)
     if (b) (void)hipFree(b);
   p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
   p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = p->d_part = p->d_psq = nullptr;
+  p->d_fix = nullptr;
 }
 
 // Kernel attributes (dynamic LDS limits) are set once per device, on first use.
@@ -209,7 +211,8 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
       {&p->d_start, H * C},       {&p->d_perm, H * N},
       {&p->d_cop, (H * C * ((size_t)desc->head_dim + 8) * 2 + 3) / 4},
       {&p->d_part, H * ((N + 255) / 256 + C) * 2 * (size_t)desc->head_dim},
-      {&p->d_psq, H * ((N + 255) / 256 + C)}};
+      {&p->d_psq, H * ((N + 255) / 256 + C)},
+      {&p->d_fix, H * N + da::kFixListOffset}};
   for (const Alloc& a : allocs) {
     if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
@@ -320,6 +323,7 @@ da_status reassign_impl(da_plan p, const void* K, const void* V, const void* cen
   a.part = reinterpret_cast<float*>(p->d_part);
   a.psq = reinterpret_cast<float*>(p->d_psq);
   a.kvar = want_variance ? key_variance_out : nullptr;
+  a.fix = p->d_fix;
   a.H = d.heads;
   a.N = d.seq_len;
   a.C = d.clusters;

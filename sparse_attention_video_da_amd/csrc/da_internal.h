@@ -31,6 +31,9 @@ struct FwdArgs {
   const float* kvar;     // [H][C] key variance for the variance-corrected cluster logits, or null
 };
 
+// Near-tie list of the bf16 assignment: a counter, then up to H * N key entries h * N + key.
+constexpr int kFixListOffset = 64;
+
 struct ReassignArgs {
   const void* K;
   const void* V;
@@ -53,6 +56,7 @@ struct ReassignArgs {
   float* part;     // workspace [H][ceil(N / 256) + C][2][D] partial sums of K and V
   float* psq;      // workspace [H][ceil(N / 256) + C] partial sums of squared key norms
   float* kvar;     // [H][C] key variance output, or null (not computed)
+  int32_t* fix;    // workspace: near-tie list, count at [0], entries from [kFixListOffset]
   int H, N, C, nb, block, mask_heads;
   int kblock;      // exact key block size S
   int ncu;         // compute units of the device (grid of the persistent assignment)

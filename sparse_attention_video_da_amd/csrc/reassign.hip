@@ -35,6 +35,10 @@ constexpr float kPosInf = __builtin_inff();
 #ifndef ASG_CH
 #define ASG_CH 128
 #endif
+// VALU instructions scheduled beside each group of the assignment's pipelined MFMAs
+#ifndef ASG_NV
+#define ASG_NV 12
+#endif
 
 // ----------------------------------------------------------------------------- 1. assign
 // bf16 distances come straight out of the MFMA. Per centroid, a pre-pass writes the product
@@ -42,17 +46,21 @@ constexpr float kPosInf = __builtin_inff();
 // bf16 parts h + m + l carry |mu|^2 (fp32, about 24 bits). Each key gets the matching row
 // [1, 1, 1, h', m', l', 0, 0] for |k|^2, so one extra 16-deep MFMA step (of D/16 + 1) leaves
 // the squared distance |k|^2 + |mu|^2 - 2 k.mu in the accumulator.
+// |mu|^2 is summed in fp64 (the squares of bf16 values are exact there, the sum nearly so),
+// so the three parts carry it to about 2^-24 relative. The kernel also clears
+// the counter of the near-tie list that the assignment fills.
 template <int D>
 __global__ void __launch_bounds__(256)
 centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__ mup,
-                         uint16_t* __restrict__ aug, int C) {
+                         uint16_t* __restrict__ aug, int32_t* __restrict__ fix_count, int C) {
   const int h = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
+  if (h == 0 && c == 0) *fix_count = 0;
   if (c >= C) return;
   const size_t row = (size_t)h * C + c;
   const uint16_t* src = mu + row * D;
   uint16_t* dst = mup + row * D;
-  float nrm = 0.f;
+  double nrm = 0.0;
 #pragma unroll
   for (int ch = 0; ch < D / 8; ++ch) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * ch);
@@ -62,17 +70,18 @@ centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__
     for (int q = 0; q < 4; ++q) {
       const float lo = bf16_to_f32((uint16_t)(wv[q] & 0xffffu));
       const float hi = bf16_to_f32((uint16_t)(wv[q] >> 16));
-      nrm = fmaf(lo, lo, nrm);
-      nrm = fmaf(hi, hi, nrm);
+      nrm = fma((double)lo, (double)lo, nrm);
+      nrm = fma((double)hi, (double)hi, nrm);
       // -2x is exact in bf16 (finite inputs): flip the sign, double through fp32
       o[q] = (uint32_t)f32_to_bf16_rne(-2.f * lo) | ((uint32_t)f32_to_bf16_rne(-2.f * hi) << 16);
     }
     *reinterpret_cast<uint4*>(dst + 8 * ch) = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  const uint16_t n0 = f32_to_bf16_rne(nrm);
-  const float r1 = nrm - bf16_to_f32(n0);
-  const uint16_t n1 = f32_to_bf16_rne(r1);
-  const uint16_t n2 = f32_to_bf16_rne(r1 - bf16_to_f32(n1));
+  // three bf16 parts of the fp64 norm (each part rounds the remainder left by the previous)
+  const uint16_t n0 = f32_to_bf16_rne((float)nrm);
+  const double r1 = nrm - (double)bf16_to_f32(n0);
+  const uint16_t n1 = f32_to_bf16_rne((float)r1);
+  const uint16_t n2 = f32_to_bf16_rne((float)(r1 - (double)bf16_to_f32(n1)));
   constexpr uint16_t kOne = 0x3f80;
   *reinterpret_cast<uint4*>(aug + row * 8) =
       make_uint4((uint32_t)n0 | ((uint32_t)n1 << 16), (uint32_t)n2 | ((uint32_t)kOne << 16),
@@ -99,7 +108,8 @@ constexpr int kAsgKtw = 2;
 template <int D>
 __device__ __forceinline__ void assign_load_keys(const uint16_t* Kh, int key0, int N, int hl,
                                                  bf16x8 (&kreg)[kAsgKtw][D / 16],
-                                                 bf16x8 (&kaug)[kAsgKtw]) {
+                                                 bf16x8 (&kaug)[kAsgKtw],
+                                                 float (&knorm)[kAsgKtw]) {
   constexpr int DS = D / 16;
 #pragma unroll
   for (int kt = 0; kt < kAsgKtw; ++kt) {
@@ -116,6 +126,7 @@ __device__ __forceinline__ void assign_load_keys(const uint16_t* Kh, int key0, i
       }
     }
     const float nk = part + xor32(part);
+    knorm[kt] = nk;
     const __bf16 n0 = (__bf16)nk;
     const float r1 = nk - (float)n0;
     const __bf16 n1 = (__bf16)r1;
@@ -132,7 +143,8 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
                                              int l32, int hl,
                                              const bf16x8 (&kreg)[kAsgKtw][D / 16],
                                              const bf16x8 (&kaug)[kAsgKtw],
-                                             int (&bestp)[kAsgKtw], int (&bbase)[kAsgKtw]) {
+                                             int (&bestp)[kAsgKtw], int (&bbase)[kAsgKtw],
+                                             int (&secp)[kAsgKtw]) {
   constexpr int DS = D / 16;
   constexpr int KTW = kAsgKtw;
   // distance tile ct of the chunk: D/16 + 1 MFMAs per key tile
@@ -165,6 +177,19 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
 #pragma unroll
       for (int r = 1; r + 1 < 16; r += 2) m = min(m, min(pk[r], pk[r + 1]));
       m = min(m, pk[15]);
+      // second smallest of the 16 (the packed values of a lane are distinct, except masked
+      // ones, which are all the largest int): in unsigned wrap-around arithmetic pk - (m + 1)
+      // sends m to the largest value and keeps the order of the rest
+      const uint32_t m1 = (uint32_t)m + 1u;
+      uint32_t w = (uint32_t)pk[0] - m1;
+#pragma unroll
+      for (int r = 1; r + 1 < 16; r += 2)
+        w = min(w, min((uint32_t)pk[r] - m1, (uint32_t)pk[r + 1] - m1));
+      w = min(w, (uint32_t)pk[15] - m1);
+      const int sv = (int)(m1 + w);
+      // running top two over the tiles: the second is the smaller of the larger of the two
+      // minima and the two seconds
+      secp[kt] = min(max(bestp[kt], m), min(secp[kt], sv));
       if (m < bestp[kt]) {
         bestp[kt] = m;
         bbase[kt] = cbase;
@@ -206,7 +231,7 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
         for (int g = 0; g < DS + 1; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, KTW, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, ASG_NV, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -221,10 +246,33 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
   }
 }
 
-// Merge the two half-waves' minima of each key (ties to the lower centroid) and store.
+// Near ties. The squared distance |k|^2 + |mu|^2 - 2 k.mu leaves the MFMA with a rounding error
+// that scales with |k|^2 + |mu|^2, not with the distance: keys far from the origin with a close
+// second centroid can come out in the wrong order. An in-bounds check of the bf16 MFMA on
+// gfx950 shows exact products aligned to the largest of the 17 terms (16 products and the
+// accumulator) in a window of at least 25 bits, then one round-to-nearest-even: each
+// 16-deep step is off by at most 17 * 2^-25 + 2^-24 of its largest term, and every term
+// here is at most |k|^2 + |mu|^2. Over D/16 + 1 <= 9 steps, with |mu|^2 carried to 2^-24 and
+// the packed index below 2^-18 of the value, every computed distance is within
+//   E = kTieErr * (|k|^2 + max_c |mu_c|^2)  (+ 2^-18 of itself)
+// of the true one; kTieErr = 2^-17 leaves a factor of 1.5 on that model. A key whose two
+// smallest computed distances are further apart than 2E (+ the packing slack) has the true
+// nearest centroid; any other key is appended to the near-tie list, and a second kernel
+// re-measures it against every centroid in difference form, sum (k - mu)^2 in fp32 (error
+// below 1e-5 of the distance itself).
+constexpr float kTieErr = 1.0f / 131072.f;   // 2^-17
+
+// Merge the two half-waves' top two of each key (ties to the lower centroid), store the
+// nearest and append keys whose top two are too close to tell apart to the near-tie list
+// (entries h * N + key).
 __device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
-                                             const int (&bbase)[kAsgKtw], int hl, int key0,
-                                             int N, int32_t* __restrict__ assign_h) {
+                                             const int (&bbase)[kAsgKtw],
+                                             const int (&secp)[kAsgKtw],
+                                             const float (&knorm)[kAsgKtw], float mu2max,
+                                             int hl, int key0, int N, int h,
+                                             int32_t* __restrict__ assign_h,
+                                             int32_t* __restrict__ fix_count,
+                                             int32_t* __restrict__ fix_list) {
 #pragma unroll
   for (int kt = 0; kt < kAsgKtw; ++kt) {
     const int mv = bestp[kt] & ~0x1f;
@@ -232,9 +280,45 @@ __device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
     const int ov = __shfl_xor(mv, 32, 64);
     const int oc = __shfl_xor(mc, 32, 64);
     const int bi = (ov < mv || (ov == mv && oc < mc)) ? oc : mc;
+    // top two over both halves: min of the larger best and the smaller second
+    const int ob = __shfl_xor(bestp[kt], 32, 64);
+    const int os = __shfl_xor(secp[kt], 32, 64);
+    const int b1 = min(bestp[kt], ob);
+    const int b2 = min(max(bestp[kt], ob), min(secp[kt], os));
+    const float q1 = __int_as_float(b1 & ~0x1f), q2 = __int_as_float(b2 & ~0x1f);
+    const float e2 = 2.f * kTieErr * (knorm[kt] + mu2max) + 0x1p-16f * fabsf(q2);
     const int key = key0 + 32 * kt;
+    const bool near = hl == 0 && key < N && b2 != 0x7fffffff && !(q2 - q1 > e2);
     if (hl == 0 && key < N) assign_h[key] = bi;
+    // wave-compacted append: one counter update per wave
+    const uint64_t ball = __builtin_amdgcn_ballot_w64(near);
+    if (ball != 0) {
+      const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      int base = 0;
+      if (lane == 0) base = atomicAdd(fix_count, (int)__builtin_popcountll(ball));
+      base = __shfl(base, 0, 64);
+      if (near) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0u));
+        fix_list[base + below] = h * N + key;
+      }
+    }
   }
+}
+
+// Largest |mu|^2 over centroid rows [0, rows) of an LDS block of augmented rows (the three
+// bf16 parts of each norm lead the row), wave-wide.
+__device__ __forceinline__ float aug_norm_max(const char* as, int rows, int lane) {
+  float m = 0.f;
+  for (int r = lane; r < rows; r += 64) {
+    const uint4 v = *reinterpret_cast<const uint4*>(as + r * 16);
+    const float n = bf16_to_f32((uint16_t)(v.x & 0xffffu)) + bf16_to_f32((uint16_t)(v.x >> 16)) +
+                    bf16_to_f32((uint16_t)(v.y & 0xffffu));
+    m = fmaxf(m, n);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  return m;
 }
 
 // Stage centroid rows c0 .. c0 + CH - 1 of one head (rows past C re-read row C - 1; their
@@ -270,7 +354,8 @@ __device__ __forceinline__ void assign_stage(__amdgpu_buffer_rsrc_t rM, __amdgpu
 template <int D, int WAVES, int CH>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
-                   const uint16_t* __restrict__ aug, int32_t* __restrict__ assign, int N,
+                   const uint16_t* __restrict__ aug, int32_t* __restrict__ assign,
+                   int32_t* __restrict__ fix_count, int32_t* __restrict__ fix_list, int N,
                    int C) {
   constexpr int DS = D / 16;
   constexpr int NCH = D / 8;
@@ -299,21 +384,25 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
 
   bf16x8 kreg[KTW][DS];
   bf16x8 kaug[KTW];
-  assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug);
+  float knorm[KTW];
+  assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug, knorm);
 
   // The centroid chunks are staged after the key loads are issued, so waiting for a chunk
   // (vmcnt counts in issue order) never waits for more than the loads issued after it.
   assign_stage<D, CH, THREADS>(rM, rA, 0, C, tid, w, mu_s0, aug_s0);
   if (nchunks > 1) assign_stage<D, CH, THREADS>(rM, rA, CH, C, tid, w, mu_s1, aug_s1);
 
-  int bestp[KTW], bbase[KTW];
+  int bestp[KTW], bbase[KTW], secp[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
-    bestp[kt] = 0x7fffffff;
+    bestp[kt] = secp[kt] = 0x7fffffff;
     bbase[kt] = 0;
   }
+  float mu2max = 0.f;   // largest |mu|^2 of the chunks seen (for the near-tie bound)
   auto compute = [&](int ci, const char* ms, const char* as) {
-    assign_chunk<D, CH>(ms, as, ci * CH, min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase);
+    mu2max = fmaxf(mu2max, aug_norm_max(as, min(CH, C - ci * CH), lane));
+    assign_chunk<D, CH>(ms, as, ci * CH, min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase,
+                        secp);
   };
   // Chunk ci sits in buffer ci % 2. Before computing it, each thread waits only until its
   // loads of chunk ci are done (the next chunk's may still be in flight), then the
@@ -341,7 +430,8 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
       }
     }
   }
-  assign_store(bestp, bbase, hl, key0, N, assign + (size_t)h * N);
+  assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, h, assign + (size_t)h * N,
+               fix_count, fix_list);
 }
 
 // Resident form, C <= kAsgResidentRows<D> (512 at d = 128, 1024 at d = 64): the whole table
@@ -357,6 +447,7 @@ template <int D, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
                             const uint16_t* __restrict__ aug, int32_t* __restrict__ assign,
+                            int32_t* __restrict__ fix_count, int32_t* __restrict__ fix_list,
                             int H, int N, int C) {
   constexpr int DS = D / 16;
   constexpr int CH = 128;
@@ -391,24 +482,84 @@ assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __re
                                    aug_s + ci * CH * 16);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
+    const float mu2max = aug_norm_max(aug_s, C, lane);   // for the near-tie bound
     const uint16_t* Kh = K + (size_t)h * N * D;
     for (int v = u + w; v < seg_end; v += WAVES) {
       const int key0 = (v - h * upn) * 64 + l32;
       bf16x8 kreg[KTW][DS];
       bf16x8 kaug[KTW];
-      assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug);
-      int bestp[KTW], bbase[KTW];
+      float knorm[KTW];
+      assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug, knorm);
+      int bestp[KTW], bbase[KTW], secp[KTW];
 #pragma unroll
       for (int kt = 0; kt < KTW; ++kt) {
-        bestp[kt] = 0x7fffffff;
+        bestp[kt] = secp[kt] = 0x7fffffff;
         bbase[kt] = 0;
       }
       for (int ci = 0; ci < nchunks; ++ci)
         assign_chunk<D, CH>(mu_s + ci * CH * D * 2, aug_s + ci * CH * 16, ci * CH,
-                            min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase);
-      assign_store(bestp, bbase, hl, key0, N, assign + (size_t)h * N);
+                            min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase, secp);
+      assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, h, assign + (size_t)h * N,
+                   fix_count, fix_list);
     }
     u = seg_end;
+  }
+}
+
+// Near-tie re-measurement (see kTieErr): every key on the list against every centroid of its
+// head in difference form, sum over dims of (k - mu)^2 in fp32 (each difference of two bf16
+// values is exact, and a sum of D non-negative terms keeps its relative error below
+// D * 2^-24, far inside the 1e-4 band); the nearest wins, ties to the lowest index. One wave
+// per listed key, lane l taking centroids l, l + 64, ...; a fixed grid walks the list, whose
+// length the assignment left in fix_count.
+template <int D>
+__global__ void __launch_bounds__(256)
+near_tie_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mu,
+                const int32_t* __restrict__ fix_count, const int32_t* __restrict__ fix_list,
+                int32_t* __restrict__ assign, int N, int C) {
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;
+  const int n = *fix_count;
+  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += nw) {
+    const int e = fix_list[i];
+    const int h = e / N, key = e - h * N;
+    const uint4* kr = reinterpret_cast<const uint4*>(K + ((size_t)h * N + key) * D);
+    uint4 kw[D / 8];
+#pragma unroll
+    for (int ch = 0; ch < D / 8; ++ch) kw[ch] = kr[ch];
+    float best = kPosInf;
+    int bc = 0;
+    for (int c = lane; c < C; c += 64) {
+      const uint4* mr = reinterpret_cast<const uint4*>(mu + ((size_t)h * C + c) * D);
+      float acc = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < D / 8; ++ch) {
+        const uint4 mv = mr[ch];
+        const uint32_t kv[4] = {kw[ch].x, kw[ch].y, kw[ch].z, kw[ch].w};
+        const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float d0 = __uint_as_float(kv[q] << 16) - __uint_as_float(mw[q] << 16);
+          const float d1 = __uint_as_float(kv[q] & 0xffff0000u) - __uint_as_float(mw[q] & 0xffff0000u);
+          acc = fmaf(d0, d0, acc);
+          acc = fmaf(d1, d1, acc);
+        }
+      }
+      if (acc < best) {   // centroids ascend within a lane: the first of equals is kept
+        best = acc;
+        bc = c;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ob = __shfl_xor(best, o, 64);
+      const int oc = __shfl_xor(bc, o, 64);
+      if (ob < best || (ob == best && oc < bc)) {
+        best = ob;
+        bc = oc;
+      }
+    }
+    if (lane == 0) assign[(size_t)h * N + key] = bc;
   }
 }
 
@@ -856,17 +1007,24 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
   {
     uint16_t* mup = a.cop;
     uint16_t* aug = a.cop + (size_t)a.H * a.C * D;
+    int32_t* fix_count = a.fix;
+    int32_t* fix_list = a.fix + kFixListOffset;
     hipLaunchKernelGGL((centroid_operands_kernel<D>), dim3((a.C + 255) / 256, a.H), dim3(256), 0,
-                       s, static_cast<const uint16_t*>(a.mu_in), mup, aug, a.C);
+                       s, static_cast<const uint16_t*>(a.mu_in), mup, aug, fix_count, a.C);
     if (a.C <= kAsgResidentRows<D>) {
       hipLaunchKernelGGL((assign_resident_bf16_kernel<D, 8>), dim3(a.ncu), dim3(8 * 64), 0, s,
-                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, a.H, a.N, a.C);
+                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, fix_count,
+                         fix_list, a.H, a.N, a.C);
     } else {
       constexpr int AW = ASG_WAVES;
       hipLaunchKernelGGL((assign_bf16_kernel<D, AW, ASG_CH>),
                          dim3((a.N + AW * 64 - 1) / (AW * 64), a.H), dim3(AW * 64), 0, s,
-                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, a.N, a.C);
+                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, fix_count,
+                         fix_list, a.N, a.C);
     }
+    hipLaunchKernelGGL((near_tie_kernel<D>), dim3(2 * a.ncu), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.mu_in),
+                       fix_count, fix_list, a.assign, a.N, a.C);
   }
   else
     hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,

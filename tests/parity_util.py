@@ -162,8 +162,8 @@ def rows_of(qblocks: List[int], block: int, n: int) -> np.ndarray:
 # one BLAS thread each; they never touch the GPU) while the test process drives the GPU.
 # A worker regenerates its head from the seeded generator (and its drift steps) instead of
 # receiving the tensors, so only caches, counts and masks cross the process boundary.
-_REF_KEYS = ("assign", "gap", "d1", "sizes", "counts", "mu1", "vbar", "mu1_exact", "vbar_exact",
-             "kvar")
+_REF_KEYS = ("assign", "gap", "d1", "d2", "sizes", "counts", "mu1", "vbar", "mu1_exact",
+             "vbar_exact", "kvar")
 _HEAD_CACHE = {}
 
 

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from datagen import get_config, make_layer, drift_layer
+from datagen import get_config, make_layer
 from parity_util import (OraclePool, check_forward, check_reassign_head, from_dev, rows_of,
                          say, store64, to_dev, torch_mod)
 
@@ -116,21 +116,6 @@ def test_full_layer_variance(lib, pool):
                     dtype=cfg.dtype)
     _step(lib, plan, cfg, L, L["cache_init"], 0, pool, _sample_qblocks(cfg, 8, 13),
           "hunyuan13b_bf16 var", variance=True)
-    plan.close()
-
-
-def test_extreme_cache_four_steps(lib, pool):
-    """1% density, C = 512: four denoising steps, K and V drift each step; the oracle's
-    refreshed cache of every head is carried to the next step (teacher forcing)."""
-    cfg = get_config("extreme_cache_bf16")
-    L = make_layer(cfg, threads=16)
-    plan = lib.Plan(cfg.heads, cfg.seq_len, cfg.head_dim, cfg.block, cfg.clusters, L["mask"],
-                    dtype=cfg.dtype)
-    qblocks = _sample_qblocks(cfg, 8, 22)
-    mu = L["cache_init"].copy()
-    for step in range(cfg.steps):
-        L = drift_layer(cfg, L, step, threads=16)
-        mu = _step(lib, plan, cfg, L, mu, step + 1, pool, qblocks, f"extreme step {step}")
     plan.close()
 
 

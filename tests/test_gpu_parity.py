@@ -166,6 +166,59 @@ def test_small_budget_config(lib):
     _run_case(lib, L, L["cache_init"], L["mask"], _cfgd(cfg), "small_budget_bf16")
 
 
+# ----------------------------------------------------------------- keys far from the origin
+@pytest.mark.parametrize("name", ["offset_keys_bf16", "offset_keys_wide_bf16",
+                                  "offset_keys_d64_bf16"])
+def test_offset_keys_assignment_is_exact_outside_the_band(lib, name):
+    """Tight clusters around centres shifted far from the origin (|k|^2 some 1e3-1e4 times
+    the nearest squared distance): distances taken as |k|^2 + |mu|^2 - 2 k.mu in fp32 carry
+    rounding errors that scale with |k|^2, not with the distances, so the assignment must
+    still be bit-exact wherever the oracle's top-two gap is outside the band (resident
+    table at d = 128 and d = 64, streamed table at C = 1024). Cache warmed by 3 oracle Lloyd
+    iterations so many keys have a close second centroid."""
+    cfg = get_config(name)
+    L = make_layer(cfg)
+    mu0 = np.stack([store64(O.lloyd_warmup(O.to_f64(L["K"][h], "bf16"),
+                                           O.to_f64(L["cache_init"][h], "bf16"), 3, "bf16"),
+                            "bf16") for h in range(cfg.heads)])
+    _run_case(lib, L, mu0, L["mask"], _cfgd(cfg), name)
+
+
+def test_duplicate_centroids_go_to_the_lowest_index(lib):
+    """A cache holding some centroids twice (identical rows): every key nearest to such a
+    centroid has an exact tie, and the assignment must take the lower index of the pair (the
+    near-tie re-measurement breaks equal distances towards the lowest index). Resident table
+    (C = 256) and streamed table (C = 1024), d = 128."""
+    torch = torch_mod()
+    for C in (256, 1024):
+        L, cache = _random_layer(150 + C, 2, 6000, 128, "bf16", C, G=C // 4, sigma=0.2)
+        dup = np.arange(C // 2, C, 3)          # higher index copies a lower one
+        src = dup - C // 2
+        cache[:, dup] = cache[:, src]
+        nb = -(-6000 // 128)
+        mask = np.zeros((1, nb, nb), np.uint8)
+        np.fill_diagonal(mask[0], 1)
+        say(f"[case] duplicate centroids: C={C}, {len(dup)} duplicated")
+        plan = lib.Plan(2, 6000, 128, 128, C, mask, dtype="bf16")
+        out = plan.reassign(to_dev(L["K"], "bf16"), to_dev(L["V"], "bf16"), to_dev(cache, "bf16"))
+        torch.cuda.synchronize()
+        a = out["assign"].cpu().numpy()
+        hit = np.isin(a, dup)
+        assert not hit.any(), f"C={C}: {int(hit.sum())} keys took the higher copy of a centroid"
+        got = {"assign": a, "sizes": out["sizes"].cpu().numpy(),
+               "counts": out["counts"].cpu().numpy(),
+               "centroids": from_dev(out["centroids"], "bf16"),
+               "mean_values": from_dev(out["mean_values"], "bf16")}
+        for h in range(2):
+            K64 = O.to_f64(L["K"][h], "bf16")
+            used = np.isin(O.assign(K64, O.to_f64(cache[h], "bf16"))[0], src).sum()
+            say(f"  head {h}: {int(used)} keys nearest to a duplicated centroid")
+            check_reassign_head(K64, O.to_f64(L["V"][h], "bf16"), O.to_f64(cache[h], "bf16"),
+                                mask[0], 128, "bf16", {k: v[h] for k, v in got.items()},
+                                f"duplicates C={C} head {h}")
+        plan.close()
+
+
 # ----------------------------------------------------------------- ragged / edge shapes
 @pytest.mark.parametrize("d,B,dtype,N", [(128, 128, "bf16", 1000), (128, 128, "bf16", 850),
                                          (64, 128, "bf16", 850), (128, 64, "bf16", 1000),
