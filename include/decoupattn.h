@@ -137,6 +137,24 @@ DA_API da_status da_reassign(da_plan plan, const void* K, const void* V,
                              int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
                              void* stream);
 
+/* da_reassign for callers that cannot allocate or may not touch the plan's workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation, arguments, outputs and errors as da_reassign, with its scratch (histograms,
+ * the cluster-sorted key order, partial sums, distance operands, the near-tie list) taken
+ * from a static device array of 64 MiB that the library holds on every device it runs on
+ * until the process ends, instead of the plan's workspace. Nothing is allocated, freed or
+ * synchronised. A plan whose reassignment workspace exceeds 64 MiB is rejected with
+ * DA_ERR_UNSUPPORTED before anything is enqueued (the workspace takes about
+ * H * (nb * C * 5 + N * 8 + (N / 256 + C) * (8 d + 4) + C * (2 d + 20)) bytes).
+ * All calls on one device share that array: calls whose executions overlap on a device
+ * (two streams, or two host threads) race and give undefined results; calls ordered on
+ * one stream are safe, and each call rewrites everything it reads from the array. */
+DA_API da_status da_reassign_noalloc(da_plan plan, const void* K, const void* V,
+                                     const void* centroids_in, void* centroids_out,
+                                     void* mean_values_out, int32_t* assign_out,
+                                     int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                                     void* stream);
+
 /* Decoupled sparse attention forward (abstract: exact attention on the fixed blocks,
  * cluster compensation of every other key, one fused kernel).
  *   Q, K, V        [H][N][d] (device).

@@ -22,8 +22,8 @@ DA_DTYPE_F32, DA_DTYPE_BF16 = 0, 1
 DTYPES = {"f32": DA_DTYPE_F32, "bf16": DA_DTYPE_BF16}
 
 EXPORTED = ("da_plan_create", "da_plan_destroy", "da_reassign", "da_forward", "da_reassign_var",
-            "da_forward_var", "da_plan_info", "da_plan_exact_lists", "da_validate_desc",
-            "da_status_str", "da_version")
+            "da_forward_var", "da_reassign_noalloc", "da_plan_info", "da_plan_exact_lists",
+            "da_validate_desc", "da_status_str", "da_version")
 
 
 class da_desc(ctypes.Structure):
@@ -63,6 +63,7 @@ def _load() -> ctypes.CDLL:
         "da_reassign": ([vp] + [vp] * 9, ctypes.c_int),
         "da_forward": ([vp] + [vp] * 9, ctypes.c_int),
         "da_reassign_var": ([vp] + [vp] * 10, ctypes.c_int),
+        "da_reassign_noalloc": ([vp] + [vp] * 9, ctypes.c_int),
         "da_forward_var": ([vp] + [vp] * 10, ctypes.c_int),
         "da_plan_info": ([vp, i32p, i64p, i64p], ctypes.c_int),
         "da_plan_exact_lists": ([vp, ctypes.c_int32, i32p, i32p], ctypes.c_int),
@@ -124,6 +125,13 @@ def da_reassign(handle, K, V, centroids_in, centroids_out, mean_values_out, assi
                 cluster_sizes_out, qblock_counts_out, stream) -> int:
     return int(_lib.da_reassign(handle, K, V, centroids_in, centroids_out, mean_values_out,
                                 assign_out, cluster_sizes_out, qblock_counts_out, stream))
+
+
+def da_reassign_noalloc(handle, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
+                        cluster_sizes_out, qblock_counts_out, stream) -> int:
+    return int(_lib.da_reassign_noalloc(handle, K, V, centroids_in, centroids_out,
+                                        mean_values_out, assign_out, cluster_sizes_out,
+                                        qblock_counts_out, stream))
 
 
 def da_forward(handle, Q, K, V, centroids, mean_values, qblock_counts, O, lse_out,
@@ -243,9 +251,11 @@ class Plan:
         return ctypes.c_void_p(s.cuda_stream)
 
     def reassign(self, K, V, centroids_in, out: Optional[Dict] = None, stream=None,
-                 variance: bool = False):
+                 variance: bool = False, noalloc: bool = False):
         """One Reassign Cache step. Returns dict(centroids, mean_values, assign, sizes, counts),
-        plus `variance` ([H][C] float32 key variance, da_reassign_var) when variance=True."""
+        plus `variance` ([H][C] float32 key variance, da_reassign_var) when variance=True.
+        noalloc=True runs da_reassign_noalloc (the library's static scratch instead of the
+        plan's workspace; pass `out` to allocate nothing on this side either)."""
         torch = _torch()
         H, N, d, C, nb = self.heads, self.seq_len, self.head_dim, self.clusters, self.num_blocks
         self._check("K", K, (H, N, d))
@@ -273,12 +283,19 @@ class Plan:
         args = (self._h, _ptr(K), _ptr(V), _ptr(centroids_in), _ptr(out["centroids"]),
                 _ptr(out["mean_values"]), _ptr(out["assign"]), _ptr(out["sizes"]),
                 _ptr(out["counts"]))
+        if variance and noalloc:
+            raise ValueError("the variance outputs have no allocation-free entry point")
         if variance:
             st = da_reassign_var(*args, _ptr(out["variance"]), self._stream(stream))
+            name = "da_reassign_var"
+        elif noalloc:
+            st = da_reassign_noalloc(*args, self._stream(stream))
+            name = "da_reassign_noalloc"
         else:
             st = da_reassign(*args, self._stream(stream))
+            name = "da_reassign"
         if st != DA_OK:
-            raise DAError(st, "da_reassign_var" if variance else "da_reassign")
+            raise DAError(st, name)
         return out
 
     def forward(self, Q, K, V, centroids, mean_values, counts, out=None, lse=False,

@@ -40,14 +40,7 @@ struct da_plan_s {
   int32_t* d_col = nullptr;
   int32_t* d_prowptr = nullptr;
   int32_t* d_pcol = nullptr;
-  int32_t* d_hist = nullptr;
-  int32_t* d_off = nullptr;
-  int32_t* d_start = nullptr;
-  int32_t* d_perm = nullptr;
-  int32_t* d_cop = nullptr;
-  int32_t* d_part = nullptr;
-  int32_t* d_psq = nullptr;
-  int32_t* d_fix = nullptr;   // near-tie list of the bf16 assignment
+  void* d_ws = nullptr;          // reassignment workspace (layout: workspace_layout)
   int64_t bytes = 0;
   int32_t ncu = 0;   // compute units of the plan's device
   int device = 0;
@@ -94,14 +87,41 @@ da_status check_desc(const da_desc* d) {
 }
 
 void destroy_device(da_plan_s* p) {
-  int32_t* bufs[] = {p->d_rowptr, p->d_col,   p->d_prowptr, p->d_pcol,
-                     p->d_hist,   p->d_off,   p->d_start,   p->d_perm, p->d_cop,
-                     p->d_part,   p->d_psq,   p->d_fix};
-  for (int32_t* b : bufs)
+  void* bufs[] = {p->d_rowptr, p->d_col, p->d_prowptr, p->d_pcol, p->d_ws};
+  for (void* b : bufs)
     if (b) (void)hipFree(b);
   p->d_rowptr = p->d_col = p->d_prowptr = p->d_pcol = nullptr;
-  p->d_hist = p->d_off = p->d_start = p->d_perm = p->d_cop = p->d_part = p->d_psq = nullptr;
-  p->d_fix = nullptr;
+  p->d_ws = nullptr;
+}
+
+// Reassignment workspace of a layer shape, carved from one device buffer (each part 256-byte
+// aligned): byte histograms [H][nb][C], column offsets [H][nb][C], cluster starts [H][C], the
+// sorted order [H][N], the bf16 distance operands [H][C][d + 8], fp32 partial sums
+// [H][ceil(N/256) + C][2][d] and squared norms [H][ceil(N/256) + C], the near-tie list.
+struct WorkspaceLayout {
+  size_t hist, off, start, perm, cop, part, psq, fix, total;
+};
+
+WorkspaceLayout workspace_layout(const da_desc& d, int32_t nb) {
+  const size_t H = d.heads, N = d.seq_len, C = d.clusters, D = d.head_dim;
+  const size_t nseg = (N + 255) / 256;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = at;
+    at += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  WorkspaceLayout w;
+  w.hist = take(H * nb * C);
+  w.off = take(H * nb * C * 4);
+  w.start = take(H * C * 4);
+  w.perm = take(H * N * 4);
+  w.cop = take(H * C * (D + 8) * 2);
+  w.part = take(H * (nseg + C) * 2 * D * 4);
+  w.psq = take(H * (nseg + C) * 4);
+  w.fix = take((H * N + da::kFixListOffset) * 4);
+  w.total = at;
+  return w;
 }
 
 // Kernel attributes (dynamic LDS limits) are set once per device, on first use.
@@ -114,6 +134,7 @@ hipError_t prepare_device(int dev) {
     if (x == dev) return hipSuccess;
   hipError_t e = da::prepare_forward_kernels();
   if (e == hipSuccess) e = da::prepare_reassign_kernels();
+  if (e == hipSuccess) e = da::scratch_setup(dev);
   if (e == hipSuccess) g_prepared.push_back(dev);
   return e;
 }
@@ -202,25 +223,22 @@ DA_API da_status da_plan_create(const da_desc* desc, const uint8_t* mask, da_pla
     return DA_ERR_DEVICE;
   }
 
-  const size_t H = desc->heads, N = desc->seq_len, C = desc->clusters;
   const size_t n_rowptr = p->rowptr.size(), n_col = std::max<size_t>(1, p->col.size());
   const size_t n_prowptr = p->prowptr.size(), n_pcol = std::max<size_t>(1, p->pcol.size());
-  struct Alloc { int32_t** ptr; size_t n; } allocs[] = {
-      {&p->d_rowptr, n_rowptr},   {&p->d_col, n_col},   {&p->d_prowptr, n_prowptr},
-      {&p->d_pcol, n_pcol},       {&p->d_hist, (H * nb * C + 3) / 4}, {&p->d_off, H * nb * C},
-      {&p->d_start, H * C},       {&p->d_perm, H * N},
-      {&p->d_cop, (H * C * ((size_t)desc->head_dim + 8) * 2 + 3) / 4},
-      {&p->d_part, H * ((N + 255) / 256 + C) * 2 * (size_t)desc->head_dim},
-      {&p->d_psq, H * ((N + 255) / 256 + C)},
-      {&p->d_fix, H * N + da::kFixListOffset}};
+  struct Alloc { void** ptr; size_t bytes; } allocs[] = {
+      {reinterpret_cast<void**>(&p->d_rowptr), n_rowptr * 4},
+      {reinterpret_cast<void**>(&p->d_col), n_col * 4},
+      {reinterpret_cast<void**>(&p->d_prowptr), n_prowptr * 4},
+      {reinterpret_cast<void**>(&p->d_pcol), n_pcol * 4},
+      {&p->d_ws, workspace_layout(*desc, nb).total}};
   for (const Alloc& a : allocs) {
-    if (hipMalloc(reinterpret_cast<void**>(a.ptr), a.n * sizeof(int32_t)) != hipSuccess) {
+    if (hipMalloc(a.ptr, a.bytes) != hipSuccess) {
       (void)hipGetLastError();
       destroy_device(p);
       delete p;
       return DA_ERR_OUT_OF_MEMORY;
     }
-    p->bytes += (int64_t)(a.n * sizeof(int32_t));
+    p->bytes += (int64_t)a.bytes;
   }
   if (hipMemcpy(p->d_rowptr, p->rowptr.data(), n_rowptr * sizeof(int32_t),
                 hipMemcpyHostToDevice) != hipSuccess ||
@@ -275,10 +293,13 @@ DA_API da_status da_plan_exact_lists(da_plan p, int32_t mh, int32_t* rowptr, int
 
 namespace {
 
+// The reassignment runs in the plan's workspace, or (use_scratch) in the library's static
+// scratch of the plan's device, which must hold the plan's workspace layout.
 da_status reassign_impl(da_plan p, const void* K, const void* V, const void* centroids_in,
                         void* centroids_out, void* mean_values_out, int32_t* assign_out,
                         int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
-                        float* key_variance_out, bool want_variance, void* stream) {
+                        float* key_variance_out, bool want_variance, bool use_scratch,
+                        void* stream) {
   if (p == nullptr || K == nullptr || V == nullptr || centroids_in == nullptr ||
       centroids_out == nullptr || mean_values_out == nullptr || assign_out == nullptr ||
       cluster_sizes_out == nullptr || qblock_counts_out == nullptr ||
@@ -301,6 +322,14 @@ da_status reassign_impl(da_plan p, const void* K, const void* V, const void* cen
   for (int i = 0; i < 6; ++i)
     if (out_bytes[i] && overlap(centroids_in, cache_bytes, outs[i], out_bytes[i]))
       return DA_ERR_INVALID_ARGUMENT;
+  const WorkspaceLayout wl = workspace_layout(d, p->nb);
+  char* ws = static_cast<char*>(p->d_ws);
+  if (use_scratch) {
+    void* sp = nullptr;
+    if (wl.total > da::kScratchBytes) return DA_ERR_UNSUPPORTED;
+    if (da::scratch_address(p->device, &sp) != hipSuccess || sp == nullptr) return DA_ERR_DEVICE;
+    ws = static_cast<char*>(sp);
+  }
   da::ReassignArgs a{};
   a.K = K;
   a.V = V;
@@ -315,15 +344,15 @@ da_status reassign_impl(da_plan p, const void* K, const void* V, const void* cen
   a.prowptr = p->d_prowptr;
   a.pcol = p->d_pcol;
   a.npairs = p->npairs;
-  a.hist = reinterpret_cast<uint8_t*>(p->d_hist);
-  a.off = p->d_off;
-  a.start = p->d_start;
-  a.perm = p->d_perm;
-  a.cop = reinterpret_cast<uint16_t*>(p->d_cop);
-  a.part = reinterpret_cast<float*>(p->d_part);
-  a.psq = reinterpret_cast<float*>(p->d_psq);
+  a.hist = reinterpret_cast<uint8_t*>(ws + wl.hist);
+  a.off = reinterpret_cast<int32_t*>(ws + wl.off);
+  a.start = reinterpret_cast<int32_t*>(ws + wl.start);
+  a.perm = reinterpret_cast<int32_t*>(ws + wl.perm);
+  a.cop = reinterpret_cast<uint16_t*>(ws + wl.cop);
+  a.part = reinterpret_cast<float*>(ws + wl.part);
+  a.psq = reinterpret_cast<float*>(ws + wl.psq);
   a.kvar = want_variance ? key_variance_out : nullptr;
-  a.fix = p->d_fix;
+  a.fix = reinterpret_cast<int32_t*>(ws + wl.fix);
   a.H = d.heads;
   a.N = d.seq_len;
   a.C = d.clusters;
@@ -391,7 +420,16 @@ DA_API da_status da_reassign(da_plan p, const void* K, const void* V, const void
                              int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
                              void* stream) {
   return reassign_impl(p, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
-                       cluster_sizes_out, qblock_counts_out, nullptr, false, stream);
+                       cluster_sizes_out, qblock_counts_out, nullptr, false, false, stream);
+}
+
+DA_API da_status da_reassign_noalloc(da_plan p, const void* K, const void* V,
+                                     const void* centroids_in, void* centroids_out,
+                                     void* mean_values_out, int32_t* assign_out,
+                                     int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
+                                     void* stream) {
+  return reassign_impl(p, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
+                       cluster_sizes_out, qblock_counts_out, nullptr, false, true, stream);
 }
 
 DA_API da_status da_reassign_var(da_plan p, const void* K, const void* V,
@@ -400,7 +438,8 @@ DA_API da_status da_reassign_var(da_plan p, const void* K, const void* V,
                                  int32_t* cluster_sizes_out, int32_t* qblock_counts_out,
                                  float* key_variance_out, void* stream) {
   return reassign_impl(p, K, V, centroids_in, centroids_out, mean_values_out, assign_out,
-                       cluster_sizes_out, qblock_counts_out, key_variance_out, true, stream);
+                       cluster_sizes_out, qblock_counts_out, key_variance_out, true, false,
+                       stream);
 }
 
 DA_API da_status da_forward(da_plan p, const void* Q, const void* K, const void* V,

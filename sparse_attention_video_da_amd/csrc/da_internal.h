@@ -69,4 +69,11 @@ hipError_t launch_reassign(const ReassignArgs& a, int head_dim, bool bf16, hipSt
 // One-time per-process kernel attribute setup (dynamic LDS limits).
 hipError_t prepare_kernels();
 
+// Static device scratch of da_reassign_noalloc: kScratchBytes per device, in the library's
+// code object. scratch_setup (called once per device, with that device current) records
+// its device address; scratch_address returns it (hipErrorNotReady before set-up).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_setup(int device);
+hipError_t scratch_address(int device, void** out);
+
 }  // namespace da

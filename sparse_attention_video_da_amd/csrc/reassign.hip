@@ -23,6 +23,10 @@
 //   7. counts        n[b][c] = size[c] - sum over b's exact blocks of hist[kb][c], per pair
 //                    (with key blocks smaller than the query blocks: size[c] minus the
 //                    exact keys of cluster c, read from the assignments).
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "da_device.h"
 #include "da_internal.h"
 
@@ -989,6 +993,43 @@ counts_keys_kernel(const int32_t* __restrict__ assign, const int32_t* __restrict
     dst[c] = cnt_lds[c];
     if (has1) dst[C + c] = cnt_lds[C + c];
   }
+}
+
+// ----------------------------------------------------------------------------- scratch
+// Workspace of da_reassign_noalloc, for callers that cannot allocate: a file-scope device
+// array that every GPU running the library holds until the process ends. Host code never
+// passes its name to a kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device, and that pointer is what the
+// kernels receive. Every call on one device shares the array; calls that overlap on a
+// device race.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void*>> g_scratch_ptr;   // (device, device address)
+}  // namespace
+
+hipError_t scratch_setup(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (const auto& e : g_scratch_ptr)
+    if (e.first == device) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (err != hipSuccess) return err;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr.emplace_back(device, ptr);
+  return hipSuccess;
+}
+
+hipError_t scratch_address(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (const auto& e : g_scratch_ptr)
+    if (e.first == device) {
+      *out = e.second;
+      return hipSuccess;
+    }
+  *out = nullptr;
+  return hipErrorNotReady;
 }
 
 // ----------------------------------------------------------------------------- launch

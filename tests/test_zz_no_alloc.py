@@ -1,0 +1,92 @@
+"""da_reassign_noalloc (the static-scratch variant of da_reassign) against da_reassign through the
+C ABI: two calls in a row on the same device, the second with a smaller layer (other H, N, d,
+C), and a plan whose workspace exceeds the static scratch rejected before anything runs. The
+two entry points share their kernels, so every output must be identical bit for bit."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from parity_util import say, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_video_da_amd as S
+    return S
+
+
+def _layer(seed, H, N, d, C, G):
+    rng = np.random.default_rng(seed)
+    from datagen import f32_to_bf16_bits
+    cen = rng.standard_normal((G, d)).astype(np.float32)
+    K = cen[rng.integers(0, G, (H, N))] + np.float32(0.25) * rng.standard_normal((H, N, d)).astype(np.float32)
+    V = rng.standard_normal((H, N, d)).astype(np.float32)
+    Kb, Vb = f32_to_bf16_bits(K), f32_to_bf16_bits(V)
+    cache = np.stack([Kb[h][np.sort(rng.choice(N, C, replace=False))] for h in range(H)])
+    return Kb, Vb, cache
+
+
+def _outputs(lib, plan, H, N, d, C):
+    torch = torch_mod()
+    nb = plan.num_blocks
+    return {"centroids": torch.empty((H, C, d), dtype=torch.bfloat16, device="cuda"),
+            "mean_values": torch.empty((H, C, d), dtype=torch.bfloat16, device="cuda"),
+            "assign": torch.full((H, N), -7, dtype=torch.int32, device="cuda"),
+            "sizes": torch.full((H, C), -7, dtype=torch.int32, device="cuda"),
+            "counts": torch.full((H, nb, C), -7, dtype=torch.int32, device="cuda")}
+
+
+@pytest.mark.parametrize("order", ["noalloc_first", "plan_first"])
+def test_noalloc_matches_reassign_on_two_calls(lib, order):
+    torch = torch_mod()
+    cases = [(4, 9000, 128, 128, 512, 7), (2, 2500, 64, 64, 100, 8)]   # second is smaller
+    for i, (H, N, d, B, C, seed) in enumerate(cases):
+        Kb, Vb, cache = _layer(seed, H, N, d, C, G=C // 2)
+        nb = -(-N // B)
+        rng = np.random.default_rng(seed + 100)
+        mask = (rng.random((1, nb, nb)) < 0.2).astype(np.uint8)
+        np.fill_diagonal(mask[0], 1)
+        say(f"[case] no-alloc call {i}: H={H} N={N} d={d} C={C} ({order})")
+        plan = lib.Plan(H, N, d, B, C, mask, dtype="bf16")
+        K, V, mu = to_dev(Kb, "bf16"), to_dev(Vb, "bf16"), to_dev(cache, "bf16")
+        a, b = _outputs(lib, plan, H, N, d, C), _outputs(lib, plan, H, N, d, C)
+        if order == "noalloc_first":
+            plan.reassign(K, V, mu, out=b, noalloc=True)
+            plan.reassign(K, V, mu, out=a)
+        else:
+            plan.reassign(K, V, mu, out=a)
+            plan.reassign(K, V, mu, out=b, noalloc=True)
+        torch.cuda.synchronize()
+        for k in a:
+            x, y = a[k], b[k]
+            if x.dtype == torch.bfloat16:
+                x, y = x.view(torch.int16), y.view(torch.int16)
+            assert torch.equal(x, y), f"call {i}: {k} differs between the entry points"
+        assert int(a["assign"].min()) >= 0 and int(a["counts"].min()) >= 0
+        plan.close()
+
+
+def test_noalloc_rejects_a_workspace_beyond_the_scratch(lib):
+    torch = torch_mod()
+    H, N, d, B, C = 2, 65536, 64, 64, 8192     # workspace about 2 * 1024 * 8192 * 5 B = 84 MB
+    mask = np.zeros((1, N // B, N // B), np.uint8)
+    np.fill_diagonal(mask[0], 1)
+    plan = lib.Plan(H, N, d, B, C, mask, dtype="bf16")
+    K = torch.zeros((H, N, d), dtype=torch.bfloat16, device="cuda")
+    mu = torch.zeros((H, C, d), dtype=torch.bfloat16, device="cuda")
+    out = _outputs(lib, plan, H, N, d, C)
+    st = lib.da_reassign_noalloc(plan._h, K.data_ptr(), K.data_ptr(), mu.data_ptr(),
+                                 out["centroids"].data_ptr(), out["mean_values"].data_ptr(),
+                                 out["assign"].data_ptr(), out["sizes"].data_ptr(),
+                                 out["counts"].data_ptr(),
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == lib.DA_ERR_UNSUPPORTED
+    assert int(out["assign"].min()) == -7 and int(out["assign"].max()) == -7   # nothing ran
+    plan.close()
