@@ -145,7 +145,7 @@ DA_API da_status da_reassign(da_plan plan, const void* K, const void* V,
  * until the process ends, instead of the plan's workspace. Nothing is allocated, freed or
  * synchronised. A plan whose reassignment workspace exceeds 64 MiB is rejected with
  * DA_ERR_UNSUPPORTED before anything is enqueued (the workspace takes about
- * H * (nb * C * 5 + N * 8 + (N / 256 + C) * (8 d + 4) + C * (2 d + 20)) bytes).
+ * H * (nb * C * 5 + N * 12 + (N / 256 + C) * (8 d + 4) + C * (2 d + 20)) bytes).
  * All calls on one device share that array: calls whose executions overlap on a device
  * (two streams, or two host threads) race and give undefined results; calls ordered on
  * one stream are safe, and each call rewrites everything it reads from the array. */

@@ -119,7 +119,7 @@ WorkspaceLayout workspace_layout(const da_desc& d, int32_t nb) {
   w.cop = take(H * C * (D + 8) * 2);
   w.part = take(H * (nseg + C) * 2 * D * 4);
   w.psq = take(H * (nseg + C) * 4);
-  w.fix = take((H * N + da::kFixListOffset) * 4);
+  w.fix = take((da::fix_list_offset((int)H) + 2 * H * N) * 4);
   w.total = at;
   return w;
 }

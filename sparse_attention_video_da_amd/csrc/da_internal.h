@@ -31,8 +31,10 @@ struct FwdArgs {
   const float* kvar;     // [H][C] key variance for the variance-corrected cluster logits, or null
 };
 
-// Near-tie list of the bf16 assignment: a counter, then up to H * N key entries h * N + key.
-constexpr int kFixListOffset = 64;
+// Near-tie lists of the bf16 assignment: one counter per head (H ints, padded to 64), then per
+// head up to N entries (key, smallest packed distance) as int2, at int offset
+// fix_list_offset(H).
+inline size_t fix_list_offset(int heads) { return (size_t)(heads + 63) / 64 * 64; }
 
 struct ReassignArgs {
   const void* K;
@@ -56,7 +58,7 @@ struct ReassignArgs {
   float* part;     // workspace [H][ceil(N / 256) + C][2][D] partial sums of K and V
   float* psq;      // workspace [H][ceil(N / 256) + C] partial sums of squared key norms
   float* kvar;     // [H][C] key variance output, or null (not computed)
-  int32_t* fix;    // workspace: near-tie list, count at [0], entries from [kFixListOffset]
+  int32_t* fix;    // workspace: near-tie counters [H], lists [H][N] int2 (fix_list_offset)
   int H, N, C, nb, block, mask_heads;
   int kblock;      // exact key block size S
   int ncu;         // compute units of the device (grid of the persistent assignment)

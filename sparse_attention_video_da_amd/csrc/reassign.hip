@@ -51,15 +51,15 @@ constexpr float kPosInf = __builtin_inff();
 // [1, 1, 1, h', m', l', 0, 0] for |k|^2, so one extra 16-deep MFMA step (of D/16 + 1) leaves
 // the squared distance |k|^2 + |mu|^2 - 2 k.mu in the accumulator.
 // |mu|^2 is summed in fp64 (the squares of bf16 values are exact there, the sum nearly so),
-// so the three parts carry it to about 2^-24 relative. The kernel also clears
-// the counter of the near-tie list that the assignment fills.
+// so the three parts carry it to about 2^-24 relative. The kernel also clears the
+// per-head counters of the near-tie lists that the assignment fills.
 template <int D>
 __global__ void __launch_bounds__(256)
 centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__ mup,
                          uint16_t* __restrict__ aug, int32_t* __restrict__ fix_count, int C) {
   const int h = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  if (h == 0 && c == 0) *fix_count = 0;
+  if (c == 0) fix_count[h] = 0;
   if (c >= C) return;
   const size_t row = (size_t)h * C + c;
   const uint16_t* src = mu + row * D;
@@ -91,6 +91,10 @@ centroid_operands_kernel(const uint16_t* __restrict__ mu, uint16_t* __restrict__
       make_uint4((uint32_t)n0 | ((uint32_t)n1 << 16), (uint32_t)n2 | ((uint32_t)kOne << 16),
                  (uint32_t)kOne | ((uint32_t)kOne << 16), 0u);
 }
+
+__device__ __forceinline__ int min3i(int a, int b, int c) { return min(a, min(b, c)); }
+// median of three (compiled to one v_med3_i32)
+__device__ __forceinline__ int med3i(int a, int b, int c) { return max(min(a, b), min(max(a, b), c)); }
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -177,20 +181,21 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
         pk[r] = (int)((__float_as_uint(acc[kt][r]) & ~0x1fu) | (uint32_t)(8 * (r >> 2) + (r & 3)));
         if (ragged && cbase + 8 * (r >> 2) + 4 * hl + (r & 3) >= limit) pk[r] = 0x7fffffff;
       }
-      int m = pk[0];
+      // smallest and second smallest of the 16 by a network of 3-way mins and medians: the
+      // median of three is their second smallest; five groups of three plus pk[15] give six
+      // minima, whose own top two (two more groups of three) and the groups' seconds give the
+      // tile's second (the smaller of the minima's second and the winning group's second,
+      // which is the smallest group second that can matter)
+      int gm[5], gs[5];
 #pragma unroll
-      for (int r = 1; r + 1 < 16; r += 2) m = min(m, min(pk[r], pk[r + 1]));
-      m = min(m, pk[15]);
-      // second smallest of the 16 (the packed values of a lane are distinct, except masked
-      // ones, which are all the largest int): in unsigned wrap-around arithmetic pk - (m + 1)
-      // sends m to the largest value and keeps the order of the rest
-      const uint32_t m1 = (uint32_t)m + 1u;
-      uint32_t w = (uint32_t)pk[0] - m1;
-#pragma unroll
-      for (int r = 1; r + 1 < 16; r += 2)
-        w = min(w, min((uint32_t)pk[r] - m1, (uint32_t)pk[r + 1] - m1));
-      w = min(w, (uint32_t)pk[15] - m1);
-      const int sv = (int)(m1 + w);
+      for (int g = 0; g < 5; ++g) {
+        gm[g] = min3i(pk[3 * g], pk[3 * g + 1], pk[3 * g + 2]);
+        gs[g] = med3i(pk[3 * g], pk[3 * g + 1], pk[3 * g + 2]);
+      }
+      const int a1 = min3i(gm[0], gm[1], gm[2]), a2 = med3i(gm[0], gm[1], gm[2]);
+      const int c1 = min3i(gm[3], gm[4], pk[15]), c2 = med3i(gm[3], gm[4], pk[15]);
+      const int m = min(a1, c1);
+      const int sv = min(min3i(max(a1, c1), a2, c2), min3i(min3i(gs[0], gs[1], gs[2]), gs[3], gs[4]));
       // running top two over the tiles: the second is the smaller of the larger of the two
       // minima and the two seconds
       secp[kt] = min(max(bestp[kt], m), min(secp[kt], sv));
@@ -254,29 +259,38 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
 // that scales with |k|^2 + |mu|^2, not with the distance: keys far from the origin with a close
 // second centroid can come out in the wrong order. An in-bounds check of the bf16 MFMA on
 // gfx950 shows exact products aligned to the largest of the 17 terms (16 products and the
-// accumulator) in a window of at least 25 bits, then one round-to-nearest-even: each
-// 16-deep step is off by at most 17 * 2^-25 + 2^-24 of its largest term, and every term
-// here is at most |k|^2 + |mu|^2. Over D/16 + 1 <= 9 steps, with |mu|^2 carried to 2^-24 and
-// the packed index below 2^-18 of the value, every computed distance is within
+// accumulator) and kept down to 2^-24 of its leading power of two (a term one binade lower is
+// dropped), then one round-to-nearest-even. Each 16-deep step is therefore off by less than
+// 17 truncations and a rounding, 18 * 2^-24 of its largest term, and every term here is at
+// most |k|^2 + |mu|^2. Over D/16 + 1 <= 9 steps, with |mu|^2 carried to 2^-24 and the packed
+// index below 2^-18 of the value, every computed distance is within
 //   E = kTieErr * (|k|^2 + max_c |mu_c|^2)  (+ 2^-18 of itself)
-// of the true one; kTieErr = 2^-17 leaves a factor of 1.5 on that model. A key whose two
-// smallest computed distances are further apart than 2E (+ the packing slack) has the true
-// nearest centroid; any other key is appended to the near-tie list, and a second kernel
-// re-measures it against every centroid in difference form, sum (k - mu)^2 in fp32 (error
-// below 1e-5 of the distance itself).
-constexpr float kTieErr = 1.0f / 131072.f;   // 2^-17
+// of the true one, with kTieErr = 2^-16 (162 * 2^-24 < 2^-16 by a factor of 1.6). A key whose
+// two smallest computed distances are further apart than 2E (+ the packing slack) has the
+// true nearest centroid; any other key is listed with its smallest computed distance, and a
+// second kernel re-measures it: every centroid whose computed distance lies within 2E of that
+// smallest is a candidate (no other can be the nearest), and each candidate's distance is
+// taken again as an fp32 sum of squared differences (error below 1e-5 of the distance).
+constexpr float kTieErr = 1.0f / 65536.f;   // 2^-16
+
+// Upper limit of the computed distance of any centroid that could be the nearest of a listed
+// key: its smallest packed distance (low index bits cleared), plus 2E, plus the packing slack.
+__device__ __forceinline__ float near_tie_limit(int b1, float knorm, float mu2max) {
+  const float q1 = __int_as_float(b1 & ~0x1f);
+  return q1 + 2.f * kTieErr * (knorm + mu2max) + 0x1p-16f * fabsf(q1);
+}
 
 // Merge the two half-waves' top two of each key (ties to the lower centroid), store the
-// nearest and append keys whose top two are too close to tell apart to the near-tie list
-// (entries h * N + key).
+// nearest and append keys whose top two are too close to tell apart to the head's near-tie
+// list, entries (key, smallest packed distance).
 __device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
                                              const int (&bbase)[kAsgKtw],
                                              const int (&secp)[kAsgKtw],
                                              const float (&knorm)[kAsgKtw], float mu2max,
-                                             int hl, int key0, int N, int h,
+                                             int hl, int key0, int N,
                                              int32_t* __restrict__ assign_h,
-                                             int32_t* __restrict__ fix_count,
-                                             int32_t* __restrict__ fix_list) {
+                                             int32_t* __restrict__ fix_count_h,
+                                             int2* __restrict__ fix_list_h) {
 #pragma unroll
   for (int kt = 0; kt < kAsgKtw; ++kt) {
     const int mv = bestp[kt] & ~0x1f;
@@ -289,22 +303,23 @@ __device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
     const int os = __shfl_xor(secp[kt], 32, 64);
     const int b1 = min(bestp[kt], ob);
     const int b2 = min(max(bestp[kt], ob), min(secp[kt], os));
-    const float q1 = __int_as_float(b1 & ~0x1f), q2 = __int_as_float(b2 & ~0x1f);
-    const float e2 = 2.f * kTieErr * (knorm[kt] + mu2max) + 0x1p-16f * fabsf(q2);
     const int key = key0 + 32 * kt;
-    const bool near = hl == 0 && key < N && b2 != 0x7fffffff && !(q2 - q1 > e2);
+    // every other centroid's computed distance is at least the second's (low bits cleared):
+    // past the limit, none of them can be the nearest
+    const bool near = hl == 0 && key < N && b2 != 0x7fffffff &&
+                      !(__int_as_float(b2 & ~0x1f) > near_tie_limit(b1, knorm[kt], mu2max));
     if (hl == 0 && key < N) assign_h[key] = bi;
     // wave-compacted append: one counter update per wave
     const uint64_t ball = __builtin_amdgcn_ballot_w64(near);
     if (ball != 0) {
       const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
       int base = 0;
-      if (lane == 0) base = atomicAdd(fix_count, (int)__builtin_popcountll(ball));
+      if (lane == 0) base = atomicAdd(fix_count_h, (int)__builtin_popcountll(ball));
       base = __shfl(base, 0, 64);
       if (near) {
         const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0u));
-        fix_list[base + below] = h * N + key;
+        fix_list_h[base + below] = make_int2(key, b1);
       }
     }
   }
@@ -359,7 +374,7 @@ template <int D, int WAVES, int CH>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
                    const uint16_t* __restrict__ aug, int32_t* __restrict__ assign,
-                   int32_t* __restrict__ fix_count, int32_t* __restrict__ fix_list, int N,
+                   int32_t* __restrict__ fix_count, int2* __restrict__ fix_list, int N,
                    int C) {
   constexpr int DS = D / 16;
   constexpr int NCH = D / 8;
@@ -434,8 +449,8 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
       }
     }
   }
-  assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, h, assign + (size_t)h * N,
-               fix_count, fix_list);
+  assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, assign + (size_t)h * N,
+               fix_count + h, fix_list + (size_t)h * N);
 }
 
 // Resident form, C <= kAsgResidentRows<D> (512 at d = 128, 1024 at d = 64): the whole table
@@ -451,7 +466,7 @@ template <int D, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
                             const uint16_t* __restrict__ aug, int32_t* __restrict__ assign,
-                            int32_t* __restrict__ fix_count, int32_t* __restrict__ fix_list,
+                            int32_t* __restrict__ fix_count, int2* __restrict__ fix_list,
                             int H, int N, int C) {
   constexpr int DS = D / 16;
   constexpr int CH = 128;
@@ -503,30 +518,192 @@ assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __re
       for (int ci = 0; ci < nchunks; ++ci)
         assign_chunk<D, CH>(mu_s + ci * CH * D * 2, aug_s + ci * CH * 16, ci * CH,
                             min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase, secp);
-      assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, h, assign + (size_t)h * N,
-                   fix_count, fix_list);
+      assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, assign + (size_t)h * N,
+                   fix_count + h, fix_list + (size_t)h * N);
     }
     u = seg_end;
   }
 }
 
-// Near-tie re-measurement (see kTieErr): every key on the list against every centroid of its
-// head in difference form, sum over dims of (k - mu)^2 in fp32 (each difference of two bf16
-// values is exact, and a sum of D non-negative terms keeps its relative error below
-// D * 2^-24, far inside the 1e-4 band); the nearest wins, ties to the lowest index. One wave
-// per listed key, lane l taking centroids l, l + 64, ...; a fixed grid walks the list, whose
-// length the assignment left in fix_count.
+// Exact squared distance of a full key row (global) to centroid c of an LDS table of -2 mu rows
+// (swizzled as assign_stage stores them): sum over dims of (k + m/2)^2 = (k - mu)^2 in fp32.
+// Each difference of two bf16 values is exact, and a sum of D non-negative terms keeps its
+// relative error below D * 2^-24 (under 1e-5 of the distance, far inside the 1e-4 band).
+template <int D>
+__device__ __forceinline__ float exact_sqdist(const uint4* __restrict__ krow, const char* ms,
+                                              int c) {
+  float acc = 0.f;
+#pragma unroll 2
+  for (int ch = 0; ch < D / 8; ++ch) {
+    const uint4 kv = krow[ch];
+    const uint4 mv = *reinterpret_cast<const uint4*>(ms + swz_byte<D>(c, ch));
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+    const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float d0 = __uint_as_float(kw[q] << 16) + 0.5f * __uint_as_float(mw[q] << 16);
+      const float d1 = __uint_as_float(kw[q] & 0xffff0000u) + 0.5f * __uint_as_float(mw[q] & 0xffff0000u);
+      acc = fmaf(d0, d0, acc);
+      acc = fmaf(d1, d1, acc);
+    }
+  }
+  return acc;
+}
+
+// Near-tie re-measurement with the head's table resident in LDS (C <= kAsgResidentRows<D>).
+// The listed keys of each head, 64 to a wave, go through the same matrix-core distances as
+// the assignment; every centroid whose distance is within the key's candidate limit
+// (near_tie_limit of its listed smallest) is re-measured exactly, the smallest exact distance
+// wins, ties to the lowest index. Persistent grid over the units of 64 listed keys of all
+// heads, table reloaded where a workgroup's range enters the next head.
+template <int D, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
+                         const uint16_t* __restrict__ aug, const int32_t* __restrict__ fix_count,
+                         const int2* __restrict__ fix_list, int32_t* __restrict__ assign, int H,
+                         int N, int C) {
+  constexpr int DS = D / 16;
+  constexpr int CH = 128;
+  constexpr int ROWS = kAsgResidentRows<D>;
+  constexpr int THREADS = WAVES * 64;
+  constexpr int KTW = kAsgKtw;
+  __shared__ __attribute__((aligned(256))) char mu_s[ROWS * D * 2];
+  __shared__ __attribute__((aligned(16))) char aug_s[ROWS * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+  const int nchunks = (C + CH - 1) / CH;
+  long long U = 0;   // units of 64 listed keys, over all heads
+  for (int h = 0; h < H; ++h) U += (__builtin_amdgcn_readfirstlane(fix_count[h]) + 63) / 64;
+  const int G = gridDim.x;
+  long long u = U * blockIdx.x / G;
+  const long long u_end = U * (blockIdx.x + 1) / G;
+  int h = 0;
+  long long hbase = 0;   // first unit of head h
+  while (u < u_end) {
+    int nh = __builtin_amdgcn_readfirstlane(fix_count[h]);
+    while (u >= hbase + (nh + 63) / 64) {   // the head holding unit u
+      hbase += (nh + 63) / 64;
+      ++h;
+      nh = __builtin_amdgcn_readfirstlane(fix_count[h]);
+    }
+    const long long seg_end = min(u_end, hbase + (nh + 63) / 64);
+    const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(mup + (size_t)h * C * D), (short)0, C * D * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(aug + (size_t)h * C * 8), (short)0, C * 16, kBufferWord3);
+    __builtin_amdgcn_s_barrier();   // every wave is done with the previous head's table
+    for (int ci = 0; ci < nchunks; ++ci)
+      assign_stage<D, CH, THREADS>(rM, rA, ci * CH, C, tid, w, mu_s + ci * CH * D * 2,
+                                   aug_s + ci * CH * 16);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    const float mu2max = aug_norm_max(aug_s, C, lane);
+    const uint16_t* Kh = K + (size_t)h * N * D;
+    const int2* lh = fix_list + (size_t)h * N;
+    for (long long v = u + w; v < seg_end; v += WAVES) {
+      const int e0 = (int)(v - hbase) * 64;
+      int key[KTW], b1[KTW];
+      bf16x8 kreg[KTW][DS];
+      bf16x8 kaug[KTW];
+      float knorm[KTW], lim[KTW], bd[KTW];
+      int bc[KTW];
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        const int e = e0 + 32 * kt + l32;
+        const int2 ent = e < nh ? lh[e] : make_int2(-1, 0);
+        key[kt] = ent.x;
+        b1[kt] = ent.y;
+        float part = 0.f;
+#pragma unroll
+        for (int s_ = 0; s_ < DS; ++s_) {
+          kreg[kt][s_] = key[kt] >= 0
+              ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key[kt] * D + 16 * s_ + 8 * hl)
+              : bf16x8{};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float x = (float)kreg[kt][s_][q];
+            part = fmaf(x, x, part);
+          }
+        }
+        const float nk = part + xor32(part);
+        knorm[kt] = nk;
+        const __bf16 n0 = (__bf16)nk;
+        const float r1 = nk - (float)n0;
+        const __bf16 n1 = (__bf16)r1;
+        const __bf16 n2 = (__bf16)(r1 - (float)n1);
+        const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
+        kaug[kt] = hl == 0 ? bf16x8{one, one, one, n0, n1, n2, zero, zero} : bf16x8{};
+        lim[kt] = near_tie_limit(b1[kt], nk, mu2max);
+        bd[kt] = kPosInf;
+        bc[kt] = 0x7fffffff;
+      }
+      for (int ct = 0; ct < (C + 31) / 32; ++ct) {
+        f32x16 acc[KTW];
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) acc[kt] = f32x16{};
+#pragma unroll
+        for (int s_ = 0; s_ < DS; ++s_) {
+          const bf16x8 a = lds_read_b128(mu_s, swz_byte<D>(32 * ct + l32, 2 * s_ + hl));
+#pragma unroll
+          for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kreg[kt][s_], acc[kt]);
+        }
+        const bf16x8 a = lds_read_b128(aug_s, (32 * ct + l32) * 16);
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kaug[kt], acc[kt]);
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) {
+          uint32_t cand = 0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * ct + 8 * (r >> 2) + 4 * hl + (r & 3);
+            cand |= (key[kt] >= 0 && c < C && acc[kt][r] <= lim[kt]) ? (1u << r) : 0u;
+          }
+          while (cand != 0) {   // rare: only keys near a tie, only centroids near the nearest
+            const int r = __builtin_ctz(cand);
+            cand &= cand - 1;
+            const int c = 32 * ct + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const float dx = exact_sqdist<D>(
+                reinterpret_cast<const uint4*>(Kh + (size_t)key[kt] * D), mu_s, c);
+            if (dx < bd[kt] || (dx == bd[kt] && c < bc[kt])) {
+              bd[kt] = dx;
+              bc[kt] = c;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        const float od = __shfl_xor(bd[kt], 32, 64);
+        const int oc = __shfl_xor(bc[kt], 32, 64);
+        const int best = (od < bd[kt] || (od == bd[kt] && oc < bc[kt])) ? oc : bc[kt];
+        if (hl == 0 && key[kt] >= 0) assign[(size_t)h * N + key[kt]] = best;
+      }
+    }
+    u = seg_end;
+  }
+}
+
+// Near-tie re-measurement when the table does not fit in LDS (C > kAsgResidentRows<D>): every
+// listed key against every centroid of its head, exactly (exact_sqdist's arithmetic with the
+// centroid rows read from global memory); ties to the lowest index. One wave per listed key,
+// lane l taking centroids l, l + 64, ...; a fixed grid walks the lists of all heads.
 template <int D>
 __global__ void __launch_bounds__(256)
 near_tie_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mu,
-                const int32_t* __restrict__ fix_count, const int32_t* __restrict__ fix_list,
-                int32_t* __restrict__ assign, int N, int C) {
+                const int32_t* __restrict__ fix_count, const int2* __restrict__ fix_list,
+                int32_t* __restrict__ assign, int H, int N, int C) {
   const int lane = threadIdx.x & 63;
   const int nw = gridDim.x * 4;
-  const int n = *fix_count;
-  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += nw) {
-    const int e = fix_list[i];
-    const int h = e / N, key = e - h * N;
+  int total = 0;
+  for (int h = 0; h < H; ++h) total += fix_count[h];
+  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < total; i += nw) {
+    int h = 0, e = i;
+    while (e >= fix_count[h]) e -= fix_count[h++];
+    const int key = fix_list[(size_t)h * N + e].x;
     const uint4* kr = reinterpret_cast<const uint4*>(K + ((size_t)h * N + key) * D);
     uint4 kw[D / 8];
 #pragma unroll
@@ -1049,23 +1226,26 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
     uint16_t* mup = a.cop;
     uint16_t* aug = a.cop + (size_t)a.H * a.C * D;
     int32_t* fix_count = a.fix;
-    int32_t* fix_list = a.fix + kFixListOffset;
+    int2* fix_list = reinterpret_cast<int2*>(a.fix + fix_list_offset(a.H));
     hipLaunchKernelGGL((centroid_operands_kernel<D>), dim3((a.C + 255) / 256, a.H), dim3(256), 0,
                        s, static_cast<const uint16_t*>(a.mu_in), mup, aug, fix_count, a.C);
     if (a.C <= kAsgResidentRows<D>) {
       hipLaunchKernelGGL((assign_resident_bf16_kernel<D, 8>), dim3(a.ncu), dim3(8 * 64), 0, s,
                          static_cast<const uint16_t*>(a.K), mup, aug, a.assign, fix_count,
                          fix_list, a.H, a.N, a.C);
+      hipLaunchKernelGGL((near_tie_resident_kernel<D, 8>), dim3(a.ncu), dim3(8 * 64), 0, s,
+                         static_cast<const uint16_t*>(a.K), mup, aug, fix_count, fix_list,
+                         a.assign, a.H, a.N, a.C);
     } else {
       constexpr int AW = ASG_WAVES;
       hipLaunchKernelGGL((assign_bf16_kernel<D, AW, ASG_CH>),
                          dim3((a.N + AW * 64 - 1) / (AW * 64), a.H), dim3(AW * 64), 0, s,
                          static_cast<const uint16_t*>(a.K), mup, aug, a.assign, fix_count,
                          fix_list, a.N, a.C);
+      hipLaunchKernelGGL((near_tie_kernel<D>), dim3(2 * a.ncu), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.mu_in),
+                         fix_count, fix_list, a.assign, a.H, a.N, a.C);
     }
-    hipLaunchKernelGGL((near_tie_kernel<D>), dim3(2 * a.ncu), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.mu_in),
-                       fix_count, fix_list, a.assign, a.N, a.C);
   }
   else
     hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,
