@@ -57,6 +57,8 @@ def parse():
                     help="skip the per-step chain of a workload with denoising steps")
     ap.add_argument("--variance", action="store_true",
                     help="time the variance-corrected step (da_reassign_var + da_forward_var)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured bf16 MFMA and HBM copy peaks")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -78,6 +80,73 @@ def load_traffic(workload: str):
     if t.get("forward_source_sha") != forward_source_sha() or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+REASSIGN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "reassign_hunyuan13b_bf16_traffic.json")
+REASSIGN_SRC = os.path.join(ROOT, "sparse_attention_video_da_amd", "csrc", "reassign.hip")
+PEAK_LIB = os.path.join(ROOT, "sparse_attention_video_da_amd", "lib", "libdapeak.so")
+
+
+def source_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_reassign_traffic(workload: str):
+    """HBM bytes per reassign step (all its kernels) from the committed counter summary, or
+    None when missing, for another workload, or taken on a different reassign source."""
+    try:
+        t = json.load(open(REASSIGN_TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("reassign_source_sha") != source_sha(REASSIGN_SRC) or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_step")
+
+
+def measured_peaks(torch):
+    """bf16 MFMA peak (independent 32x32x16 chains, 4 waves per SIMD) and HBM copy rate (2 GiB
+    read + 2 GiB written per rep), timed with HIP events on the device."""
+    import ctypes
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.dapeak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    lib.dapeak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 4 * ncu
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    ms, flop = ctypes.c_float(), ctypes.c_double()
+    if lib.dapeak_mfma_bf16(wgs, 100000, ctypes.c_void_p(out.data_ptr()), ctypes.byref(ms),
+                            ctypes.byref(flop)) != 0:
+        return None
+    mfma_tflops = flop.value / (ms.value * 1e-3) / 1e12
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    cms = ctypes.c_float()
+    if lib.dapeak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                       nbytes, 8 * ncu, 5, ctypes.byref(cms)) != 0:
+        return None
+    copy_gbs = 2.0 * nbytes / (cms.value * 1e-3) / 1e9
+    lib.dapeak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    rout = torch.empty(8 * ncu * 256, dtype=torch.int32, device="cuda")
+    rms = ctypes.c_float()
+    if lib.dapeak_read(ctypes.c_void_p(src.data_ptr()), nbytes, 8 * ncu, 5,
+                       ctypes.c_void_p(rout.data_ptr()), ctypes.byref(rms)) != 0:
+        return None
+    read_gbs = nbytes / (rms.value * 1e-3) / 1e9
+    del src, dst, rout
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_copy_gbs": round(copy_gbs, 1),
+            "hbm_read_gbs": round(read_gbs, 1),
+            "mfma_note": "v_mfma_f32_32x32x16_bf16, 8 independent accumulators per wave, "
+                         "4 waves per SIMD",
+            "hbm_note": "2 GiB device-to-device copy (read + write bytes counted) and 2 GiB "
+                        "streaming read, 16-byte nontemporal accesses, 4 in flight a thread"}
 
 
 def cpu_model() -> str:
@@ -317,6 +386,13 @@ def main():
                 + 2.0 * H * C * d * es        # refreshed centroids + means
                 + H * nb * C * 4.0)           # counts
     traffic = load_traffic(cfg.name)
+    peaks = None
+    if not args.no_peaks:
+        log("[bench] measuring the bf16 MFMA and HBM copy peaks ...")
+        try:
+            peaks = measured_peaks(torch)
+        except Exception as e:  # reported, never fatal
+            peaks = {"error": repr(e)}
     result = {
         "metric": "ms per attention layer + achieved MFMA bf16 TFLOPS fraction at 5% density",
         "value": round(wall_ms, 4),
@@ -342,7 +418,25 @@ def main():
                      cfg.dtype == "bf16" else f"fwd_f32_kernel<{d},{B}>",
                      "flops_per_launch": exact_flop,
                      "flops_basis": "exact-block MFMA work, 4*B*S*d per (query block, exact "
-                                    "key block of S keys) pair"},
+                                    "key block of S keys) pair",
+                     "forward_source_sha": source_sha(FORWARD_SRC),
+                     "frac_of_measured_peak": (round(achieved / peaks["mfma_bf16_tflops"], 4)
+                                               if peaks and "mfma_bf16_tflops" in peaks
+                                               else None)},
+        "reassign_roofline": {
+            "bound": "hbm", "achieved": round(re_bytes / (re_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(re_bytes / (re_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_reassign_traffic(cfg.name),
+            "bytes_per_step": re_bytes,
+            "bytes_basis": "K and V read once, assignments, refreshed centroids and mean values, "
+                           "counts written once",
+            "reassign_source_sha": source_sha(REASSIGN_SRC),
+            "frac_of_measured_peak": (round(re_bytes / (re_ms * 1e-3) / 1e9
+                                            / peaks["hbm_copy_gbs"], 4)
+                                      if peaks and "hbm_copy_gbs" in peaks else None),
+            "assign_mfma_flop": 2.0 * C * d * N * H},
+        "peaks_measured": peaks,
         "breakdown": {
             "forward_ms": round(fw_ms, 4), "forward_ms_median": round(fw_med, 4),
             "forward_ms_p10_p90": [round(float(np.percentile(fw_all, 10)), 4),

@@ -1,7 +1,8 @@
 """Build the HIP library in-tree: sparse_attention_video_da_amd/lib/libdecoupattn.so.
 
-Compiles every source under csrc/ for gfx950 with hipcc and links one shared library
-exporting only the C ABI declared in include/decoupattn.h.
+Compiles the attention sources under csrc/ for gfx950 with hipcc and links one shared library
+exporting only the C ABI declared in include/decoupattn.h; the benchmark's peak probe
+(csrc/peak_probe.hip) becomes lib/libdapeak.so.
 
     python sparse_attention_video_da_amd/build.py [--jobs N]
 """
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdecoupattn.so")
 SOURCES = ["api.cpp", "plan_lists.cpp", "forward.hip", "reassign.hip"]
+PEAK_SOURCE = "peak_probe.hip"
+PEAK_LIB = os.path.join(LIBDIR, "libdapeak.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -66,6 +69,11 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the benchmark's peak probe (not part of the attention library)
+    probe = compile_one(PEAK_SOURCE)
+    tmp = PEAK_LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe])
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 

@@ -81,6 +81,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Read-only, wave-uniform loads through the scalar cache.
+__device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
+  return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -78,11 +78,6 @@ struct ic {
   static constexpr int value = N;
 };
 
-// Read-only, wave-uniform loads through the scalar cache.
-__device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
-  return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
-}
-
 // The list entries of one exact tile (the first G lanes are used). A vector value, not an
 // addressable array: an array passed between the helpers below gets placed in LDS by the
 // compiler, costing LDS traffic and full waits every tile.

@@ -111,10 +111,10 @@ constexpr int kAsgKtw = 2;
 
 // This lane's keys: the B operand of D^T = mu K^T (dims 16s + 8hl .. +7), and the
 // augmented row for |k|^2 on the lower half (zero on the upper half, so whatever the
-// centroid side holds in dims 8..15 of that step contributes nothing). Keys at or past N
-// are zero.
+// centroid side holds in dims 8..15 of that step contributes nothing). The loads go through
+// a buffer resource over the head's keys (32-bit offsets; keys at or past N read as zero).
 template <int D>
-__device__ __forceinline__ void assign_load_keys(const uint16_t* Kh, int key0, int N, int hl,
+__device__ __forceinline__ void assign_load_keys(__amdgpu_buffer_rsrc_t rK, int key0, int hl,
                                                  bf16x8 (&kreg)[kAsgKtw][D / 16],
                                                  bf16x8 (&kaug)[kAsgKtw],
                                                  float (&knorm)[kAsgKtw]) {
@@ -125,8 +125,8 @@ __device__ __forceinline__ void assign_load_keys(const uint16_t* Kh, int key0, i
     float part = 0.f;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      kreg[kt][s] = key < N ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * s + 8 * hl)
-                            : bf16x8{};
+      kreg[kt][s] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rK, (key * D + 16 * s + 8 * hl) * 2, 0, 0));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = (float)kreg[kt][s][e];
@@ -290,7 +290,8 @@ __device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
                                              int hl, int key0, int N,
                                              int32_t* __restrict__ assign_h,
                                              int32_t* __restrict__ fix_count_h,
-                                             int2* __restrict__ fix_list_h) {
+                                             int2* __restrict__ fix_list_h,
+                                             uint32_t* hist_lds) {
 #pragma unroll
   for (int kt = 0; kt < kAsgKtw; ++kt) {
     const int mv = bestp[kt] & ~0x1f;
@@ -308,7 +309,11 @@ __device__ __forceinline__ void assign_store(const int (&bestp)[kAsgKtw],
     // past the limit, none of them can be the nearest
     const bool near = hl == 0 && key < N && b2 != 0x7fffffff &&
                       !(__int_as_float(b2 & ~0x1f) > near_tie_limit(b1, knorm[kt], mu2max));
-    if (hl == 0 && key < N) assign_h[key] = bi;
+    if (hl == 0 && key < N) {
+      assign_h[key] = bi;
+      // the block's cluster histogram (16-bit counters, two to a word)
+      if (hist_lds != nullptr) atomicAdd(&hist_lds[bi >> 1], 1u << (16 * (bi & 1)));
+    }
     // wave-compacted append: one counter update per wave
     const uint64_t ball = __builtin_amdgcn_ballot_w64(near);
     if (ball != 0) {
@@ -404,7 +409,9 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
   bf16x8 kreg[KTW][DS];
   bf16x8 kaug[KTW];
   float knorm[KTW];
-  assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug, knorm);
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Kh, (short)0, N * D * 2, kBufferWord3);
+  assign_load_keys<D>(rK, key0, hl, kreg, kaug, knorm);
 
   // The centroid chunks are staged after the key loads are issued, so waiting for a chunk
   // (vmcnt counts in issue order) never waits for more than the loads issued after it.
@@ -450,24 +457,26 @@ assign_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ 
     }
   }
   assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, assign + (size_t)h * N,
-               fix_count + h, fix_list + (size_t)h * N);
+               fix_count + h, fix_list + (size_t)h * N, nullptr);
 }
 
 // Resident form, C <= kAsgResidentRows<D> (512 at d = 128, 1024 at d = 64): the whole table
 // of one head stays in LDS (128 KB of operands plus the augmented rows) and the keys stream
-// past it. One workgroup of WAVES
-// waves per CU, a persistent grid: workgroup g takes units [g U / G, (g+1) U / G) of the
-// U = H * ceil(N / 64) units of 64 keys in (head, key) order, reloading the table where its
-// range enters the next head; between reloads every wave walks its own units (u = first +
-// w, + WAVES, ...) with no barrier, so one wave's key loads hide behind the others' MFMAs.
+// past it. One workgroup of WAVES waves per CU, a persistent grid: workgroup g takes units
+// [g U / G, (g+1) U / G) of the U = H * nb key blocks in (head, block) order, reloading the
+// table where its range enters the next head; between reloads every wave walks its own
+// blocks (u = first + w, + WAVES, ...) with no barrier, so one wave's key loads hide behind
+// the others' MFMAs. A wave assigns a block's keys 64 at a time and counts them per cluster
+// in its own LDS histogram (16-bit counters, LDS atomics), then stores the block's byte
+// histogram row for the refresh (the near-tie pass corrects it where it moves a key).
 template <int D>
 constexpr int kAsgResidentRows = 65536 / D;   // 128 KB of bf16 operands
-template <int D, int WAVES>
+template <int D, int WAVES, int BLK>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
                             const uint16_t* __restrict__ aug, int32_t* __restrict__ assign,
-                            int32_t* __restrict__ fix_count, int2* __restrict__ fix_list,
-                            int H, int N, int C) {
+                            uint8_t* __restrict__ hist, int32_t* __restrict__ fix_count,
+                            int2* __restrict__ fix_list, int H, int N, int C, int nb) {
   constexpr int DS = D / 16;
   constexpr int CH = 128;
   constexpr int ROWS = kAsgResidentRows<D>;
@@ -476,6 +485,7 @@ assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __re
   static_assert(ROWS % CH == 0, "whole chunks");
   __shared__ __attribute__((aligned(256))) char mu_s[ROWS * D * 2];
   __shared__ __attribute__((aligned(16))) char aug_s[ROWS * 16];
+  __shared__ uint32_t hist_s[WAVES * ROWS / 2];   // per wave: C 16-bit counters
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -483,14 +493,14 @@ assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __re
   const int hl = lane >> 5;
   const int l32 = lane & 31;
   const int nchunks = (C + CH - 1) / CH;
-  const int upn = (N + 63) / 64;   // units per head
-  const long long U = (long long)H * upn;
+  const long long U = (long long)H * nb;
   const int G = gridDim.x;
   int u = (int)(U * blockIdx.x / G);
   const int u_end = (int)(U * (blockIdx.x + 1) / G);
+  uint32_t* hs = hist_s + w * (ROWS / 2);
   while (u < u_end) {
-    const int h = u / upn;
-    const int seg_end = min(u_end, (h + 1) * upn);
+    const int h = u / nb;
+    const int seg_end = min(u_end, (h + 1) * nb);
     const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(mup + (size_t)h * C * D), (short)0, C * D * 2, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
@@ -502,42 +512,48 @@ assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __re
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     const float mu2max = aug_norm_max(aug_s, C, lane);   // for the near-tie bound
-    const uint16_t* Kh = K + (size_t)h * N * D;
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(K + (size_t)h * N * D), (short)0, N * D * 2, kBufferWord3);
     for (int v = u + w; v < seg_end; v += WAVES) {
-      const int key0 = (v - h * upn) * 64 + l32;
-      bf16x8 kreg[KTW][DS];
-      bf16x8 kaug[KTW];
-      float knorm[KTW];
-      assign_load_keys<D>(Kh, key0, N, hl, kreg, kaug, knorm);
-      int bestp[KTW], bbase[KTW], secp[KTW];
+      const int kb = v - h * nb;
+      for (int i = lane; i < (C + 1) / 2; i += 64) hs[i] = 0u;
+#pragma unroll 1
+      for (int sub = 0; sub < BLK; sub += 64) {
+        const int key0 = kb * BLK + sub + l32;
+        bf16x8 kreg[KTW][DS];
+        bf16x8 kaug[KTW];
+        float knorm[KTW];
+        assign_load_keys<D>(rK, key0, hl, kreg, kaug, knorm);
+        int bestp[KTW], bbase[KTW], secp[KTW];
 #pragma unroll
-      for (int kt = 0; kt < KTW; ++kt) {
-        bestp[kt] = secp[kt] = 0x7fffffff;
-        bbase[kt] = 0;
+        for (int kt = 0; kt < KTW; ++kt) {
+          bestp[kt] = secp[kt] = 0x7fffffff;
+          bbase[kt] = 0;
+        }
+        for (int ci = 0; ci < nchunks; ++ci)
+          assign_chunk<D, CH>(mu_s + ci * CH * D * 2, aug_s + ci * CH * 16, ci * CH,
+                              min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase, secp);
+        assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, assign + (size_t)h * N,
+                     fix_count + h, fix_list + (size_t)h * N, hs);
       }
-      for (int ci = 0; ci < nchunks; ++ci)
-        assign_chunk<D, CH>(mu_s + ci * CH * D * 2, aug_s + ci * CH * 16, ci * CH,
-                            min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase, secp);
-      assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, assign + (size_t)h * N,
-                   fix_count + h, fix_list + (size_t)h * N);
+      uint8_t* row = hist + ((size_t)h * nb + kb) * C;
+      for (int c = lane; c < C; c += 64) row[c] = (uint8_t)(hs[c >> 1] >> (16 * (c & 1)));
     }
     u = seg_end;
   }
 }
 
-// Exact squared distance of a full key row (global) to centroid c of an LDS table of -2 mu rows
+// Exact squared distance of a full key row (in registers) to centroid c of an LDS table of -2 mu rows
 // (swizzled as assign_stage stores them): sum over dims of (k + m/2)^2 = (k - mu)^2 in fp32.
 // Each difference of two bf16 values is exact, and a sum of D non-negative terms keeps its
 // relative error below D * 2^-24 (under 1e-5 of the distance, far inside the 1e-4 band).
 template <int D>
-__device__ __forceinline__ float exact_sqdist(const uint4* __restrict__ krow, const char* ms,
-                                              int c) {
+__device__ __forceinline__ float exact_sqdist(const uint4 (&kf)[D / 8], const char* ms, int c) {
   float acc = 0.f;
-#pragma unroll 2
+#pragma unroll
   for (int ch = 0; ch < D / 8; ++ch) {
-    const uint4 kv = krow[ch];
     const uint4 mv = *reinterpret_cast<const uint4*>(ms + swz_byte<D>(c, ch));
-    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+    const uint32_t kw[4] = {kf[ch].x, kf[ch].y, kf[ch].z, kf[ch].w};
     const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -560,8 +576,8 @@ template <int D, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ mup,
                          const uint16_t* __restrict__ aug, const int32_t* __restrict__ fix_count,
-                         const int2* __restrict__ fix_list, int32_t* __restrict__ assign, int H,
-                         int N, int C) {
+                         const int2* __restrict__ fix_list, int32_t* __restrict__ assign,
+                         uint8_t* __restrict__ hist, int H, int N, int C, int nb, int block) {
   constexpr int DS = D / 16;
   constexpr int CH = 128;
   constexpr int ROWS = kAsgResidentRows<D>;
@@ -641,6 +657,15 @@ near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restr
         bd[kt] = kPosInf;
         bc[kt] = 0x7fffffff;
       }
+      // phase 1: the matrix-core distances, collecting each lane's candidates (up to four;
+      // more mark the key for an exact pass over every centroid)
+      int cs[KTW][4], ncand[KTW];
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        ncand[kt] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs[kt][j] = 0;
+      }
       for (int ct = 0; ct < (C + 31) / 32; ++ct) {
         f32x16 acc[KTW];
 #pragma unroll
@@ -662,16 +687,38 @@ near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restr
             const int c = 32 * ct + 8 * (r >> 2) + 4 * hl + (r & 3);
             cand |= (key[kt] >= 0 && c < C && acc[kt][r] <= lim[kt]) ? (1u << r) : 0u;
           }
-          while (cand != 0) {   // rare: only keys near a tie, only centroids near the nearest
+          while (cand != 0) {   // rare: only centroids near the nearest of a listed key
             const int r = __builtin_ctz(cand);
             cand &= cand - 1;
             const int c = 32 * ct + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const float dx = exact_sqdist<D>(
-                reinterpret_cast<const uint4*>(Kh + (size_t)key[kt] * D), mu_s, c);
-            if (dx < bd[kt] || (dx == bd[kt] && c < bc[kt])) {
-              bd[kt] = dx;
-              bc[kt] = c;
-            }
+            const int n = ncand[kt];
+            cs[kt][0] = n == 0 ? c : cs[kt][0];
+            cs[kt][1] = n == 1 ? c : cs[kt][1];
+            cs[kt][2] = n == 2 ? c : cs[kt][2];
+            cs[kt][3] = n == 3 ? c : cs[kt][3];
+            ncand[kt] = min(n + 1, 5);
+          }
+        }
+      }
+      // phase 2: exact distances from the full key row (in registers) and the LDS table
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        if (key[kt] < 0 || ncand[kt] == 0) continue;
+        uint4 kf[D / 8];
+        const uint4* kr = reinterpret_cast<const uint4*>(Kh + (size_t)key[kt] * D);
+#pragma unroll
+        for (int ch = 0; ch < D / 8; ++ch) kf[ch] = kr[ch];
+        const int n = ncand[kt];
+        const int ncheck = n <= 4 ? n : C;   // more than four: every centroid of this half
+        for (int j = 0; j < ncheck; ++j) {
+          int c;
+          if (n <= 4) c = j == 0 ? cs[kt][0] : j == 1 ? cs[kt][1] : j == 2 ? cs[kt][2] : cs[kt][3];
+          else c = j;
+          if (n > 4 && (((c >> 2) & 1) != hl)) continue;   // the other half's centroids
+          const float dx = exact_sqdist<D>(kf, mu_s, c);
+          if (dx < bd[kt] || (dx == bd[kt] && c < bc[kt])) {
+            bd[kt] = dx;
+            bc[kt] = c;
           }
         }
       }
@@ -680,7 +727,21 @@ near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restr
         const float od = __shfl_xor(bd[kt], 32, 64);
         const int oc = __shfl_xor(bc[kt], 32, 64);
         const int best = (od < bd[kt] || (od == bd[kt] && oc < bc[kt])) ? oc : bc[kt];
-        if (hl == 0 && key[kt] >= 0) assign[(size_t)h * N + key[kt]] = best;
+        if (hl == 0 && key[kt] >= 0) {
+          int32_t* ap = assign + (size_t)h * N + key[kt];
+          const int old = *ap;
+          if (old != best) {
+            // move the key between the byte counters of its block's histogram row: the old
+            // counter holds it (no borrow), the new one stays below 256 (no carry)
+            const size_t rb = ((size_t)h * nb + key[kt] / block) * C;
+            const size_t ob = rb + old, nbt = rb + best;
+            atomicAdd(reinterpret_cast<uint32_t*>(hist + (ob & ~(size_t)3)),
+                      0u - (1u << (8 * (ob & 3))));
+            atomicAdd(reinterpret_cast<uint32_t*>(hist + (nbt & ~(size_t)3)),
+                      1u << (8 * (nbt & 3)));
+            *ap = best;
+          }
+        }
       }
     }
     u = seg_end;
@@ -799,7 +860,9 @@ block_hist_kernel(const int32_t* __restrict__ assign, uint8_t* __restrict__ hist
 }
 
 // ----------------------------------------------------------------------------- 3. col scan
-// 16 waves split the key blocks; lane = cluster. Two passes over the histograms.
+// 16 waves split the key blocks; lane = cluster. Two passes over the histograms, each with 8
+// rows' bytes in flight (the rows are independent loads; one at a time would leave every
+// wave waiting on the memory latency once per block).
 __global__ void __launch_bounds__(1024)
 col_scan_kernel(const uint8_t* __restrict__ hist, int32_t* __restrict__ off,
                 int32_t* __restrict__ sizes, int C, int nb) {
@@ -810,9 +873,19 @@ col_scan_kernel(const uint8_t* __restrict__ hist, int32_t* __restrict__ off,
   const int span = (nb + 15) / 16;
   const int kb0 = min(nb, w * span), kb1 = min(nb, kb0 + span);
   const uint8_t* col = hist + (size_t)h * nb * C + c;
+  constexpr int U = 8;
   int s = 0;
-  if (c < C)
-    for (int kb = kb0; kb < kb1; ++kb) s += col[(size_t)kb * C];
+  if (c < C) {
+    int kb = kb0;
+    for (; kb + U <= kb1; kb += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = col[(size_t)(kb + u) * C];
+#pragma unroll
+      for (int u = 0; u < U; ++u) s += v[u];
+    }
+    for (; kb < kb1; ++kb) s += col[(size_t)kb * C];
+  }
   part[w][lane] = s;
   __syncthreads();
   int pre = 0, tot = 0;
@@ -824,7 +897,18 @@ col_scan_kernel(const uint8_t* __restrict__ hist, int32_t* __restrict__ off,
   if (c < C) {
     int32_t* ocol = off + (size_t)h * nb * C + c;
     int run = pre;
-    for (int kb = kb0; kb < kb1; ++kb) {
+    int kb = kb0;
+    for (; kb + U <= kb1; kb += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = col[(size_t)(kb + u) * C];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ocol[(size_t)(kb + u) * C] = run;
+        run += v[u];
+      }
+    }
+    for (; kb < kb1; ++kb) {
       ocol[(size_t)kb * C] = run;
       run += col[(size_t)kb * C];
     }
@@ -1119,6 +1203,83 @@ counts_kernel(const uint8_t* __restrict__ hist, const int32_t* __restrict__ size
   }
 }
 
+// The same counts with 8 clusters a lane (C a multiple of 8): one wave per (pair, slab of 512
+// clusters) walks the pair's union list, reading 8 histogram bytes of each entry's row with
+// one load (a wave reads 512 consecutive bytes) and adding them into the counters of the users
+// of that entry (wave-uniform branches on the entry's user bits).
+__global__ void __launch_bounds__(256)
+counts8_kernel(const uint8_t* __restrict__ hist, const int32_t* __restrict__ sizes,
+               const int32_t* __restrict__ prowptr, const int32_t* __restrict__ pcol,
+               int32_t* __restrict__ counts, int C, int nb, int npairs, int mask_heads,
+               int nslab, int items) {
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= items) return;
+  const int lane = threadIdx.x & 63;
+  const int slab = item % nslab;
+  const int pr = (item / nslab) % npairs;
+  const int h = item / (nslab * npairs);
+  const int c = slab * 512 + lane * 8;
+  const int b0 = 2 * pr;
+  const bool has1 = b0 + 1 < nb;
+  const int mh = mask_heads == 1 ? 0 : h;
+  const int e0 = sload(prowptr, mh * (npairs + 1) + pr);
+  const int e1 = sload(prowptr, mh * (npairs + 1) + pr + 1);
+  if (c >= C) return;
+  const uint8_t* hh = hist + (size_t)h * nb * C + c;
+  int both[8], only0[8], only1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) both[j] = only0[j] = only1[j] = 0;
+  auto add = [](int (&acc)[8], uint2 v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += (v.x >> (8 * j)) & 0xff;
+      acc[4 + j] += (v.y >> (8 * j)) & 0xff;
+    }
+  };
+  constexpr int U = 8;   // entries (and their rows) in flight
+  int e = e0;
+  for (; e + U <= e1; e += U) {
+    int ent[U];
+    uint2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ent[u] = sload(pcol, e + u);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = *reinterpret_cast<const uint2*>(hh + (size_t)(ent[u] & kEntIndex) * C);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int use = (ent[u] >> kEntUse0) & 3;
+      if (use == 3) add(both, v[u]);
+      else if (use == 1) add(only0, v[u]);
+      else if (use == 2) add(only1, v[u]);
+    }
+  }
+  for (; e < e1; ++e) {
+    const int ent = sload(pcol, e);
+    const uint2 v = *reinterpret_cast<const uint2*>(hh + (size_t)(ent & kEntIndex) * C);
+    const int use = (ent >> kEntUse0) & 3;
+    if (use == 3) add(both, v);
+    else if (use == 1) add(only0, v);
+    else if (use == 2) add(only1, v);
+  }
+  const int4 sa = *reinterpret_cast<const int4*>(sizes + (size_t)h * C + c);
+  const int4 sb = *reinterpret_cast<const int4*>(sizes + (size_t)h * C + c + 4);
+  const int sz[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+  int32_t* dst0 = counts + ((size_t)h * nb + b0) * C + c;
+  int n0[8], n1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    n0[j] = sz[j] - both[j] - only0[j];
+    n1[j] = sz[j] - both[j] - only1[j];
+  }
+  *reinterpret_cast<int4*>(dst0) = make_int4(n0[0], n0[1], n0[2], n0[3]);
+  *reinterpret_cast<int4*>(dst0 + 4) = make_int4(n0[4], n0[5], n0[6], n0[7]);
+  if (has1) {
+    *reinterpret_cast<int4*>(dst0 + C) = make_int4(n1[0], n1[1], n1[2], n1[3]);
+    *reinterpret_cast<int4*>(dst0 + C + 4) = make_int4(n1[4], n1[5], n1[6], n1[7]);
+  }
+}
+
 // Counts when the exact key blocks (S keys) are smaller than the query blocks: per pair,
 // n[b][c] starts from size[c] in LDS and every key of the union list's key blocks takes one
 // off the rows of the query blocks that keep it, read straight from the assignments (4 bytes
@@ -1221,6 +1382,7 @@ static void launch_sums(const ReassignArgs& a, int nseg, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_t s) {
+  bool hist_done = false;   // the resident assignment writes the block histograms itself
   if (bf16)
   {
     uint16_t* mup = a.cop;
@@ -1230,12 +1392,18 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
     hipLaunchKernelGGL((centroid_operands_kernel<D>), dim3((a.C + 255) / 256, a.H), dim3(256), 0,
                        s, static_cast<const uint16_t*>(a.mu_in), mup, aug, fix_count, a.C);
     if (a.C <= kAsgResidentRows<D>) {
-      hipLaunchKernelGGL((assign_resident_bf16_kernel<D, 8>), dim3(a.ncu), dim3(8 * 64), 0, s,
-                         static_cast<const uint16_t*>(a.K), mup, aug, a.assign, fix_count,
-                         fix_list, a.H, a.N, a.C);
+      if (a.block == 128)
+        hipLaunchKernelGGL((assign_resident_bf16_kernel<D, 8, 128>), dim3(a.ncu), dim3(8 * 64), 0,
+                           s, static_cast<const uint16_t*>(a.K), mup, aug, a.assign, a.hist,
+                           fix_count, fix_list, a.H, a.N, a.C, a.nb);
+      else
+        hipLaunchKernelGGL((assign_resident_bf16_kernel<D, 8, 64>), dim3(a.ncu), dim3(8 * 64), 0,
+                           s, static_cast<const uint16_t*>(a.K), mup, aug, a.assign, a.hist,
+                           fix_count, fix_list, a.H, a.N, a.C, a.nb);
       hipLaunchKernelGGL((near_tie_resident_kernel<D, 8>), dim3(a.ncu), dim3(8 * 64), 0, s,
                          static_cast<const uint16_t*>(a.K), mup, aug, fix_count, fix_list,
-                         a.assign, a.H, a.N, a.C);
+                         a.assign, a.hist, a.H, a.N, a.C, a.nb, a.block);
+      hist_done = true;
     } else {
       constexpr int AW = ASG_WAVES;
       hipLaunchKernelGGL((assign_bf16_kernel<D, AW, ASG_CH>),
@@ -1251,8 +1419,9 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
     hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((a.N + 255) / 256, a.H), dim3(256), 0, s,
                        static_cast<const float*>(a.K), static_cast<const float*>(a.mu_in),
                        a.assign, a.N, a.C);
-  hipLaunchKernelGGL(block_hist_kernel, dim3(a.nb, a.H), dim3(256), a.C * sizeof(int32_t), s,
-                     a.assign, a.hist, a.N, a.C, a.nb, a.block);
+  if (!hist_done)
+    hipLaunchKernelGGL(block_hist_kernel, dim3(a.nb, a.H), dim3(256), a.C * sizeof(int32_t), s,
+                       a.assign, a.hist, a.N, a.C, a.nb, a.block);
   hipLaunchKernelGGL(col_scan_kernel, dim3((a.C + 63) / 64, a.H), dim3(1024), 0, s, a.hist,
                      a.off, a.sizes, a.C, a.nb);
   hipLaunchKernelGGL(starts_kernel, dim3(a.H), dim3(1024), 0, s, a.sizes, a.start, a.C);
@@ -1268,7 +1437,13 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
       else launch_sums<D, false, false>(a, nseg, s);
     }
   }
-  if (a.kblock == a.block)
+  if (a.kblock == a.block && a.C % 8 == 0) {
+    const int nslab = (a.C + 511) / 512;
+    const int items = a.H * a.npairs * nslab;
+    hipLaunchKernelGGL(counts8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, a.hist, a.sizes,
+                       a.prowptr, a.pcol, a.counts, a.C, a.nb, a.npairs, a.mask_heads, nslab,
+                       items);
+  } else if (a.kblock == a.block)
     hipLaunchKernelGGL(counts_kernel, dim3(a.npairs, a.H), dim3(256), 0, s, a.hist, a.sizes,
                        a.prowptr, a.pcol, a.counts, a.C, a.nb, a.npairs, a.mask_heads);
   else
