@@ -144,7 +144,91 @@ __device__ __forceinline__ void assign_load_keys(__amdgpu_buffer_rsrc_t rK, int 
   }
 }
 
-// Running packed minimum of this wave's keys over one LDS chunk of centroid operands: rows
+// Running top two (packed) of this wave's keys over one 32-centroid distance tile starting at
+// centroid cbase; centroids at or past `limit` (a ragged last tile) are excluded. Accumulator r
+// of a lane holds centroid cbase + 8(r/4) + 4hl + r%4: its distance with the tile-local index
+// 8(r/4) + r%4 packed into the 5 low mantissa bits.
+__device__ __forceinline__ void tile_top2(const f32x16 (&acc)[kAsgKtw], int cbase, bool ragged,
+                                          int limit, int hl, int (&bestp)[kAsgKtw],
+                                          int (&bbase)[kAsgKtw], int (&secp)[kAsgKtw]) {
+#pragma unroll
+  for (int kt = 0; kt < kAsgKtw; ++kt) {
+    int pk[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pk[r] = (int)((__float_as_uint(acc[kt][r]) & ~0x1fu) | (uint32_t)(8 * (r >> 2) + (r & 3)));
+      if (ragged && cbase + 8 * (r >> 2) + 4 * hl + (r & 3) >= limit) pk[r] = 0x7fffffff;
+    }
+    // smallest and second smallest of the 16 by a network of 3-way mins and medians: the
+    // median of three is their second smallest; five groups of three plus pk[15] give six
+    // minima, whose own top two (two more groups of three) and the groups' seconds give the
+    // tile's second (the smaller of the minima's second and the winning group's second,
+    // which is the smallest group second that can matter)
+    int gm[5], gs[5];
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+      gm[g] = min3i(pk[3 * g], pk[3 * g + 1], pk[3 * g + 2]);
+      gs[g] = med3i(pk[3 * g], pk[3 * g + 1], pk[3 * g + 2]);
+    }
+    const int a1 = min3i(gm[0], gm[1], gm[2]), a2 = med3i(gm[0], gm[1], gm[2]);
+    const int c1 = min3i(gm[3], gm[4], pk[15]), c2 = med3i(gm[3], gm[4], pk[15]);
+    const int m = min(a1, c1);
+    const int sv = min(min3i(max(a1, c1), a2, c2), min3i(min3i(gs[0], gs[1], gs[2]), gs[3], gs[4]));
+    // running top two over the tiles: the second is the smaller of the larger of the two
+    // minima and the two seconds
+    secp[kt] = min(max(bestp[kt], m), min(secp[kt], sv));
+    if (m < bestp[kt]) {
+      bestp[kt] = m;
+      bbase[kt] = cbase;
+    }
+  }
+}
+
+// Distance tiles of this wave's keys against the centroid rows of an LDS table (-2 mu rows
+// swizzled, then the augmented rows): D/16 + 1 MFMAs per key tile.
+template <int D>
+struct AsgTiles {
+  static constexpr int DS = D / 16;
+  const char* ms;
+  const char* as;
+  int l32, hl;
+  const bf16x8 (&kreg)[kAsgKtw][D / 16];
+  const bf16x8 (&kaug)[kAsgKtw];
+  __device__ __forceinline__ void load_ops(int ct, bf16x8 (&o)[DS + 1]) const {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) o[s] = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
+    o[DS] = lds_read_b128(as, (32 * ct + l32) * 16);
+  }
+  __device__ __forceinline__ void mfma_ops(const bf16x8 (&o)[DS + 1],
+                                           f32x16 (&acc)[kAsgKtw]) const {
+#pragma unroll
+    for (int kt = 0; kt < kAsgKtw; ++kt) acc[kt] = f32x16{};
+#pragma unroll
+    for (int s = 0; s <= DS; ++s)
+#pragma unroll
+      for (int kt = 0; kt < kAsgKtw; ++kt)
+        acc[kt] = mfma32x32x16(o[s], s < DS ? kreg[kt][s] : kaug[kt], acc[kt]);
+  }
+  __device__ __forceinline__ void tile(int ct, f32x16 (&acc)[kAsgKtw]) const {
+    bf16x8 o[DS + 1];
+    load_ops(ct, o);
+    mfma_ops(o, acc);
+  }
+};
+
+// Scheduling groups beside one tile's MFMAs: KTW MFMAs, one LDS operand read and ASG_NV VALU
+// instructions per k-step, so the next tile's products run beside this tile's argmin.
+template <int D>
+__device__ __forceinline__ void asg_sched_groups() {
+#pragma unroll
+  for (int g = 0; g < D / 16 + 1; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kAsgKtw, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, ASG_NV, 0);
+  }
+}
+
+// Running top two of this wave's keys over one LDS chunk of centroid operands: rows
 // c0 .. c0 + valid - 1 (valid <= CH), stored as the staging below lays them out.
 template <int D, int CH>
 __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int c0, int valid,
@@ -155,56 +239,7 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
                                              int (&secp)[kAsgKtw]) {
   constexpr int DS = D / 16;
   constexpr int KTW = kAsgKtw;
-  // distance tile ct of the chunk: D/16 + 1 MFMAs per key tile
-  auto tile_mfma = [&](int ct, f32x16 (&acc)[KTW]) {
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) acc[kt] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const bf16x8 a = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
-#pragma unroll
-      for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kreg[kt][s], acc[kt]);
-    }
-    const bf16x8 a = lds_read_b128(as, (32 * ct + l32) * 16);
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) acc[kt] = mfma32x32x16(a, kaug[kt], acc[kt]);
-  };
-  // running packed minimum over the tile starting at centroid cbase; centroids at or past
-  // `limit` (a ragged last tile) are excluded
-  auto tile_min = [&](const f32x16 (&acc)[KTW], int cbase, bool ragged, int limit) {
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) {
-      int pk[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // accumulator r holds centroid cbase + 8(r/4) + 4hl + r%4; pack 8(r/4) + r%4
-        pk[r] = (int)((__float_as_uint(acc[kt][r]) & ~0x1fu) | (uint32_t)(8 * (r >> 2) + (r & 3)));
-        if (ragged && cbase + 8 * (r >> 2) + 4 * hl + (r & 3) >= limit) pk[r] = 0x7fffffff;
-      }
-      // smallest and second smallest of the 16 by a network of 3-way mins and medians: the
-      // median of three is their second smallest; five groups of three plus pk[15] give six
-      // minima, whose own top two (two more groups of three) and the groups' seconds give the
-      // tile's second (the smaller of the minima's second and the winning group's second,
-      // which is the smallest group second that can matter)
-      int gm[5], gs[5];
-#pragma unroll
-      for (int g = 0; g < 5; ++g) {
-        gm[g] = min3i(pk[3 * g], pk[3 * g + 1], pk[3 * g + 2]);
-        gs[g] = med3i(pk[3 * g], pk[3 * g + 1], pk[3 * g + 2]);
-      }
-      const int a1 = min3i(gm[0], gm[1], gm[2]), a2 = med3i(gm[0], gm[1], gm[2]);
-      const int c1 = min3i(gm[3], gm[4], pk[15]), c2 = med3i(gm[3], gm[4], pk[15]);
-      const int m = min(a1, c1);
-      const int sv = min(min3i(max(a1, c1), a2, c2), min3i(min3i(gs[0], gs[1], gs[2]), gs[3], gs[4]));
-      // running top two over the tiles: the second is the smaller of the larger of the two
-      // minima and the two seconds
-      secp[kt] = min(max(bestp[kt], m), min(secp[kt], sv));
-      if (m < bestp[kt]) {
-        bestp[kt] = m;
-        bbase[kt] = cbase;
-      }
-    }
-  };
+  const AsgTiles<D> T{ms, as, l32, hl, kreg, kaug};
   constexpr int NT = CH / 32;
   if (valid == CH) {
     // full chunk, software-pipelined: the MFMAs of tile t+1 run beside the argmin of t,
@@ -212,46 +247,73 @@ __device__ __forceinline__ void assign_chunk(const char* ms, const char* as, int
     // tile t has just released
     f32x16 acc[2][KTW];
     bf16x8 ops[2][DS + 1];
-    auto load_ops = [&](int ct, bf16x8 (&o)[DS + 1]) {
-#pragma unroll
-      for (int s = 0; s < DS; ++s) o[s] = lds_read_b128(ms, swz_byte<D>(32 * ct + l32, 2 * s + hl));
-      o[DS] = lds_read_b128(as, (32 * ct + l32) * 16);
-    };
-    auto mfma_ops = [&](const bf16x8 (&o)[DS + 1], f32x16 (&acc_)[KTW]) {
-#pragma unroll
-      for (int kt = 0; kt < KTW; ++kt) acc_[kt] = f32x16{};
-#pragma unroll
-      for (int s = 0; s <= DS; ++s)
-#pragma unroll
-        for (int kt = 0; kt < KTW; ++kt)
-          acc_[kt] = mfma32x32x16(o[s], s < DS ? kreg[kt][s] : kaug[kt], acc_[kt]);
-    };
-    load_ops(0, ops[0]);
-    if (NT > 1) load_ops(1, ops[1]);
-    mfma_ops(ops[0], acc[0]);
+    T.load_ops(0, ops[0]);
+    if (NT > 1) T.load_ops(1, ops[1]);
+    T.mfma_ops(ops[0], acc[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t + 1 < NT) mfma_ops(ops[(t + 1) & 1], acc[(t + 1) & 1]);
-      if (t + 2 < NT) load_ops(t + 2, ops[t & 1]);
-      tile_min(acc[t & 1], c0 + 32 * t, false, 0);
-      if (t + 1 < NT) {
-#pragma unroll
-        for (int g = 0; g < DS + 1; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, KTW, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, ASG_NV, 0);
-        }
-      }
+      if (t + 1 < NT) T.mfma_ops(ops[(t + 1) & 1], acc[(t + 1) & 1]);
+      if (t + 2 < NT) T.load_ops(t + 2, ops[t & 1]);
+      tile_top2(acc[t & 1], c0 + 32 * t, false, 0, hl, bestp, bbase, secp);
+      if (t + 1 < NT) asg_sched_groups<D>();
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     const int ntile = (valid + 31) / 32;
     for (int ct = 0; ct < ntile; ++ct) {
       f32x16 acc[KTW];
-      tile_mfma(ct, acc);
-      tile_min(acc, c0 + 32 * ct, 32 * ct + 32 > valid, c0 + valid);
+      T.tile(ct, acc);
+      tile_top2(acc, c0 + 32 * ct, 32 * ct + 32 > valid, c0 + valid, hl, bestp, bbase, secp);
     }
+  }
+}
+
+// Running top two over a whole resident table of C centroids (rows contiguous in LDS): one
+// software pipeline across an even number of full 32-centroid tiles (no restart at chunk
+// edges), then an odd last full tile and the ragged tile of C % 32 centroids one at a time.
+template <int D>
+__device__ __forceinline__ void assign_table(const char* ms, const char* as, int C, int l32,
+                                             int hl, const bf16x8 (&kreg)[kAsgKtw][D / 16],
+                                             const bf16x8 (&kaug)[kAsgKtw],
+                                             int (&bestp)[kAsgKtw], int (&bbase)[kAsgKtw],
+                                             int (&secp)[kAsgKtw]) {
+  constexpr int DS = D / 16;
+  constexpr int KTW = kAsgKtw;
+  const AsgTiles<D> T{ms, as, l32, hl, kreg, kaug};
+  const int ntp = (C >> 5) & ~1;   // full tiles taken in pairs
+  if (ntp > 0) {
+    f32x16 acc[2][KTW];
+    bf16x8 ops[2][DS + 1];
+    T.load_ops(0, ops[0]);
+    T.load_ops(1, ops[1]);
+    T.mfma_ops(ops[0], acc[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // steady state, two tiles a trip: the argmin of tile t beside the MFMAs of tile t+1,
+    // while tile t+2's operands load into the registers tile t's MFMAs have released
+    for (int t = 0; t + 2 < ntp; t += 2) {
+      T.mfma_ops(ops[1], acc[1]);
+      T.load_ops(t + 2, ops[0]);
+      tile_top2(acc[0], 32 * t, false, 0, hl, bestp, bbase, secp);
+      asg_sched_groups<D>();
+      __builtin_amdgcn_sched_barrier(0);
+      T.mfma_ops(ops[0], acc[0]);
+      T.load_ops(t + 3, ops[1]);
+      tile_top2(acc[1], 32 * t + 32, false, 0, hl, bestp, bbase, secp);
+      asg_sched_groups<D>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the last pair: tile ntp-1's MFMAs beside tile ntp-2's argmin, then its own argmin
+    T.mfma_ops(ops[1], acc[1]);
+    tile_top2(acc[0], 32 * (ntp - 2), false, 0, hl, bestp, bbase, secp);
+    asg_sched_groups<D>();
+    __builtin_amdgcn_sched_barrier(0);
+    tile_top2(acc[1], 32 * (ntp - 1), false, 0, hl, bestp, bbase, secp);
+  }
+  for (int ct = ntp; ct < (C + 31) / 32; ++ct) {   // an odd full tile, the ragged tile
+    f32x16 acc[KTW];
+    T.tile(ct, acc);
+    tile_top2(acc, 32 * ct, 32 * ct + 32 > C, C, hl, bestp, bbase, secp);
   }
 }
 
@@ -530,9 +592,7 @@ assign_resident_bf16_kernel(const uint16_t* __restrict__ K, const uint16_t* __re
           bestp[kt] = secp[kt] = 0x7fffffff;
           bbase[kt] = 0;
         }
-        for (int ci = 0; ci < nchunks; ++ci)
-          assign_chunk<D, CH>(mu_s + ci * CH * D * 2, aug_s + ci * CH * 16, ci * CH,
-                              min(CH, C - ci * CH), l32, hl, kreg, kaug, bestp, bbase, secp);
+        assign_table<D>(mu_s, aug_s, C, l32, hl, kreg, kaug, bestp, bbase, secp);
         assign_store(bestp, bbase, secp, knorm, mu2max, hl, key0, N, assign + (size_t)h * N,
                      fix_count + h, fix_list + (size_t)h * N, hs);
       }
