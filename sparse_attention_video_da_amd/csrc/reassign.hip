@@ -787,7 +787,10 @@ near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restr
         const float od = __shfl_xor(bd[kt], 32, 64);
         const int oc = __shfl_xor(bc[kt], 32, 64);
         const int best = (od < bd[kt] || (od == bd[kt] && oc < bc[kt])) ? oc : bc[kt];
-        if (hl == 0 && key[kt] >= 0) {
+        // The key's own nearest computed distance is always within its limit, so a candidate
+        // exists; only non-finite inputs (NaN distances compare false) can leave none, and then
+        // the provisional assignment stands.
+        if (hl == 0 && key[kt] >= 0 && best >= 0 && best < C) {
           int32_t* ap = assign + (size_t)h * N + key[kt];
           const int old = *ap;
           if (old != best) {
