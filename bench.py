@@ -432,9 +432,10 @@ def main():
             "bytes_basis": "K and V read once, assignments, refreshed centroids and mean values, "
                            "counts written once",
             "reassign_source_sha": source_sha(REASSIGN_SRC),
+            # the step's bytes are nearly all reads: against the measured streaming-read rate
             "frac_of_measured_peak": (round(re_bytes / (re_ms * 1e-3) / 1e9
-                                            / peaks["hbm_copy_gbs"], 4)
-                                      if peaks and "hbm_copy_gbs" in peaks else None),
+                                            / peaks["hbm_read_gbs"], 4)
+                                      if peaks and "hbm_read_gbs" in peaks else None),
             "assign_mfma_flop": 2.0 * C * d * N * H},
         "peaks_measured": peaks,
         "breakdown": {
