@@ -109,6 +109,23 @@ constexpr int vmcnt_imm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | ((
 // winner.
 constexpr int kAsgKtw = 2;
 
+// |k|^2 of a lane's half row (D/2 bf16 values) by packed bf16 dot products, four partial
+// sums. Its rounding shifts every distance of the key alike, so it moves neither the nearest
+// centroid nor the top-two gap; the assignment and the near-tie pass must take it the same
+// way, since the pass compares its distances with the assignment's.
+template <int D>
+__device__ __forceinline__ float half_row_sq_norm(const bf16x8 (&row)[D / 16]) {
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 x = {row[s][2 * e], row[s][2 * e + 1]};
+      part[e] = __builtin_amdgcn_fdot2_f32_bf16(x, x, part[e], false);
+    }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
 // This lane's keys: the B operand of D^T = mu K^T (dims 16s + 8hl .. +7), and the
 // augmented row for |k|^2 on the lower half (zero on the upper half, so whatever the
 // centroid side holds in dims 8..15 of that step contributes nothing). The loads go through
@@ -122,18 +139,12 @@ __device__ __forceinline__ void assign_load_keys(__amdgpu_buffer_rsrc_t rK, int 
 #pragma unroll
   for (int kt = 0; kt < kAsgKtw; ++kt) {
     const int key = key0 + 32 * kt;
-    float part = 0.f;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
+    for (int s = 0; s < DS; ++s)
       kreg[kt][s] = __builtin_bit_cast(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rK, (key * D + 16 * s + 8 * hl) * 2, 0, 0));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)kreg[kt][s][e];
-        part = fmaf(x, x, part);
-      }
-    }
-    const float nk = part + xor32(part);
+    const float ps = half_row_sq_norm<D>(kreg[kt]);
+    const float nk = ps + xor32(ps);
     knorm[kt] = nk;
     const __bf16 n0 = (__bf16)nk;
     const float r1 = nk - (float)n0;
@@ -693,19 +704,13 @@ near_tie_resident_kernel(const uint16_t* __restrict__ K, const uint16_t* __restr
         const int2 ent = e < nh ? lh[e] : make_int2(-1, 0);
         key[kt] = ent.x;
         b1[kt] = ent.y;
-        float part = 0.f;
 #pragma unroll
-        for (int s_ = 0; s_ < DS; ++s_) {
+        for (int s_ = 0; s_ < DS; ++s_)
           kreg[kt][s_] = key[kt] >= 0
               ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key[kt] * D + 16 * s_ + 8 * hl)
               : bf16x8{};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float x = (float)kreg[kt][s_][q];
-            part = fmaf(x, x, part);
-          }
-        }
-        const float nk = part + xor32(part);
+        const float ps = half_row_sq_norm<D>(kreg[kt]);
+        const float nk = ps + xor32(ps);
         knorm[kt] = nk;
         const __bf16 n0 = (__bf16)nk;
         const float r1 = nk - (float)n0;
@@ -1006,19 +1011,27 @@ starts_kernel(const int32_t* __restrict__ sizes, int32_t* __restrict__ start, in
 }
 
 // ----------------------------------------------------------------------------- 5. scatter
-__global__ void __launch_bounds__(256)
+// One workgroup of `block` threads (64 or 128) per query block; a key's slot is its cluster's
+// start, plus the block's offset in that cluster, plus its rank among the block's earlier keys
+// of the cluster, so the sorted order is ascending key order within each cluster.
+__global__ void __launch_bounds__(128)
 scatter_kernel(const int32_t* __restrict__ assign, const int32_t* __restrict__ off,
                const int32_t* __restrict__ start, int32_t* __restrict__ perm, int N, int C,
                int nb, int block) {
-  __shared__ int32_t a_lds[256];
+  __shared__ int4 a_lds[32];   // the block's assignments (at most 128), four to an entry
   const int h = blockIdx.y, kb = blockIdx.x, tid = threadIdx.x;
   const int j = kb * block + tid;
   const int c = (tid < block && j < N) ? assign[(size_t)h * N + j] : -1;
-  a_lds[tid] = c;
+  reinterpret_cast<int32_t*>(a_lds)[tid] = c;
   __syncthreads();
   if (c >= 0) {
+    // rank among the block's earlier keys of the same cluster: whole entries, then the rest
     int r = 0;
-    for (int t = 0; t < tid; ++t) r += a_lds[t] == c;
+    for (int t4 = 0; t4 < (tid >> 2); ++t4) {
+      const int4 v = a_lds[t4];
+      r += (v.x == c) + (v.y == c) + (v.z == c) + (v.w == c);
+    }
+    for (int t = tid & ~3; t < tid; ++t) r += reinterpret_cast<const int32_t*>(a_lds)[t] == c;
     const int pos = start[(size_t)h * C + c] + off[((size_t)h * nb + kb) * C + c] + r;
     perm[(size_t)h * N + pos] = j;
   }
@@ -1488,7 +1501,7 @@ static hipError_t launch_reassign_t(const ReassignArgs& a, bool bf16, hipStream_
   hipLaunchKernelGGL(col_scan_kernel, dim3((a.C + 63) / 64, a.H), dim3(1024), 0, s, a.hist,
                      a.off, a.sizes, a.C, a.nb);
   hipLaunchKernelGGL(starts_kernel, dim3(a.H), dim3(1024), 0, s, a.sizes, a.start, a.C);
-  hipLaunchKernelGGL(scatter_kernel, dim3(a.nb, a.H), dim3(256), 0, s, a.assign, a.off,
+  hipLaunchKernelGGL(scatter_kernel, dim3(a.nb, a.H), dim3(a.block), 0, s, a.assign, a.off,
                      a.start, a.perm, a.N, a.C, a.nb, a.block);
   {
     const int nseg = (a.N + kSeg - 1) / kSeg;
