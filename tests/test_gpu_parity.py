@@ -219,6 +219,75 @@ def test_duplicate_centroids_go_to_the_lowest_index(lib):
         plan.close()
 
 
+@pytest.mark.parametrize("d,C", [(128, 256), (64, 512)])
+def test_many_equal_centroids_take_the_exact_pass_over_the_half(lib, d, C):
+    """Six identical copies of one centroid, all on one half-wave's side of the distance tiles
+    (centroid index c with (c >> 2) & 1 == 0): a key nearest to them has more candidates than
+    the near-tie pass keeps, so that lane re-measures every centroid of its half exactly. It
+    must still take the lowest copy, and everything else must match the oracle. Resident table
+    at d = 128 and d = 64."""
+    torch = torch_mod()
+    H, N = 2, 4000
+    L, cache = _random_layer(700 + d, H, N, d, "bf16", C, G=C // 4, sigma=0.2)
+    copies = np.array([8, 16, 24, 40, 48, 56])
+    assert np.all(((copies >> 2) & 1) == 0)
+    cache[:, copies[1:]] = cache[:, copies[:1]]
+    nb = -(-N // 128)
+    mask = np.zeros((1, nb, nb), np.uint8)
+    np.fill_diagonal(mask[0], 1)
+    say(f"[case] six equal centroids: d={d} C={C}")
+    plan = lib.Plan(H, N, d, 128, C, mask, dtype="bf16")
+    out = plan.reassign(to_dev(L["K"], "bf16"), to_dev(L["V"], "bf16"), to_dev(cache, "bf16"))
+    torch.cuda.synchronize()
+    a = out["assign"].cpu().numpy()
+    hit = np.isin(a, copies[1:])
+    assert not hit.any(), f"{int(hit.sum())} keys took a higher copy of the centroid"
+    got = {"assign": a, "sizes": out["sizes"].cpu().numpy(),
+           "counts": out["counts"].cpu().numpy(),
+           "centroids": from_dev(out["centroids"], "bf16"),
+           "mean_values": from_dev(out["mean_values"], "bf16")}
+    for h in range(H):
+        K64 = O.to_f64(L["K"][h], "bf16")
+        n8 = int((O.assign(K64, O.to_f64(cache[h], "bf16"))[0] == copies[0]).sum())
+        say(f"  head {h}: {n8} keys nearest to the repeated centroid")
+        assert n8 > 0, "the case must exercise the repeated centroid"
+        check_reassign_head(K64, O.to_f64(L["V"][h], "bf16"), O.to_f64(cache[h], "bf16"),
+                            mask[0], 128, "bf16", {k: v[h] for k, v in got.items()},
+                            f"six equal centroids d={d} head {h}")
+    plan.close()
+
+
+@pytest.mark.parametrize("C", [64, 1024])
+def test_all_centroids_equal(lib, C):
+    """Degenerate cache: every centroid the same row. Every key is an exact C-way tie, lists as
+    a near tie and re-measures every centroid; all must go to cluster 0, which takes every key,
+    while the other clusters stay empty (cached centroid kept, mean value zero, counts zero).
+    Resident (C = 64) and streamed (C = 1024) tables."""
+    torch = torch_mod()
+    H, N, d = 2, 3000, 128
+    L, cache = _random_layer(900 + C, H, N, d, "bf16", C)
+    cache[:] = cache[:, :1]
+    nb = -(-N // 128)
+    mask = np.zeros((1, nb, nb), np.uint8)
+    np.fill_diagonal(mask[0], 1)
+    say(f"[case] all centroids equal: C={C}")
+    plan = lib.Plan(H, N, d, 128, C, mask, dtype="bf16")
+    out = plan.reassign(to_dev(L["K"], "bf16"), to_dev(L["V"], "bf16"), to_dev(cache, "bf16"))
+    torch.cuda.synchronize()
+    a = out["assign"].cpu().numpy()
+    assert np.array_equal(a, np.zeros_like(a)), f"{int((a != 0).sum())} keys left cluster 0"
+    got = {"assign": a, "sizes": out["sizes"].cpu().numpy(),
+           "counts": out["counts"].cpu().numpy(),
+           "centroids": from_dev(out["centroids"], "bf16"),
+           "mean_values": from_dev(out["mean_values"], "bf16")}
+    assert np.array_equal(got["sizes"][:, 0], np.full(H, N)) and not got["sizes"][:, 1:].any()
+    for h in range(H):
+        check_reassign_head(O.to_f64(L["K"][h], "bf16"), O.to_f64(L["V"][h], "bf16"),
+                            O.to_f64(cache[h], "bf16"), mask[0], 128, "bf16",
+                            {k: v[h] for k, v in got.items()}, f"all equal C={C} head {h}")
+    plan.close()
+
+
 # ----------------------------------------------------------------- ragged / edge shapes
 @pytest.mark.parametrize("d,B,dtype,N", [(128, 128, "bf16", 1000), (128, 128, "bf16", 850),
                                          (64, 128, "bf16", 850), (128, 64, "bf16", 1000),
