@@ -120,11 +120,13 @@ DA_API da_status da_plan_destroy(da_plan plan);
  *   assign_out         [H][N] a_j = argmin_c ||k_j - mu0_c||^2 (squared Euclidean on the
  *                      stored values). fp32 plans: differences squared and summed in fp32,
  *                      equal sums go to the lowest c. bf16 plans: distances from the bf16
- *                      matrix cores with fp32 accumulation; a key whose two nearest
- *                      centroids are too close for that arithmetic to order (within a bound
- *                      proportional to 2^-17 (|k|^2 + max |mu|^2)) is re-measured as an fp32
- *                      sum of squared differences against every centroid, equal sums going
- *                      to the lowest c. Either way the chosen centroid is the nearest unless
+ *                      matrix cores with fp32 accumulation (their error grows with
+ *                      |k|^2 + |mu|^2, not with the distance); a key whose two nearest
+ *                      computed distances lie within 2^-15 (|k|^2 + max |mu|^2), plus 2^-16
+ *                      of the smaller, of each other is re-measured as an fp32 sum of squared
+ *                      differences against every centroid whose computed distance is within
+ *                      that bound of its smallest (no other can be its nearest), equal sums
+ *                      going to the lowest c. Either way the chosen centroid is the nearest unless
  *                      the two nearest lie within a relative 1e-4 of each other (then any of
  *                      them may be chosen).
  *   cluster_sizes_out  [H][C] number of keys per cluster.
