@@ -1,7 +1,8 @@
 """da_reassign_noalloc (the static-scratch variant of da_reassign) against da_reassign through the
 C ABI: two calls in a row on the same device, the second with a smaller layer (other H, N, d,
-C), and a plan whose workspace exceeds the static scratch rejected before anything runs. The
-two entry points share their kernels, so every output must be identical bit for bit."""
+C), replays of a captured HIP graph with other calls rewriting the scratch between them, and a
+plan whose workspace exceeds the static scratch rejected before anything runs. The two entry
+points share their kernels, so every output must be identical bit for bit."""
 import ctypes
 
 import numpy as np
@@ -70,6 +71,63 @@ def test_noalloc_matches_reassign_on_two_calls(lib, order):
             assert torch.equal(x, y), f"call {i}: {k} differs between the entry points"
         assert int(a["assign"].min()) >= 0 and int(a["counts"].min()) >= 0
         plan.close()
+
+
+def test_noalloc_replays_in_a_hip_graph(lib):
+    """The callers da_reassign_noalloc is for include code under HIP graph capture: capture it
+    on a side stream, then replay it three times with eager calls between the replays that
+    rewrite the shared scratch (an allocation-free call on another, larger layer, and
+    da_reassign on the captured layer). Every replay must equal the eager call bit for bit."""
+    torch = torch_mod()
+    H, N, d, B, C = 3, 5000, 128, 128, 256
+    Kb, Vb, cache = _layer(31, H, N, d, C, G=C // 2)
+    nb = -(-N // B)
+    mask = (np.random.default_rng(131).random((1, nb, nb)) < 0.2).astype(np.uint8)
+    np.fill_diagonal(mask[0], 1)
+    plan = lib.Plan(H, N, d, B, C, mask, dtype="bf16")
+    K, V, mu = to_dev(Kb, "bf16"), to_dev(Vb, "bf16"), to_dev(cache, "bf16")
+    # the other layer whose eager calls overwrite the scratch between replays
+    H2, N2, d2, C2 = 2, 9000, 64, 512
+    K2b, V2b, cache2 = _layer(32, H2, N2, d2, C2, G=C2 // 2)
+    nb2 = -(-N2 // 64)
+    mask2 = np.zeros((1, nb2, nb2), np.uint8)
+    np.fill_diagonal(mask2[0], 1)
+    plan2 = lib.Plan(H2, N2, d2, 64, C2, mask2, dtype="bf16")
+    K2, V2, mu2 = to_dev(K2b, "bf16"), to_dev(V2b, "bf16"), to_dev(cache2, "bf16")
+    out2 = _outputs(lib, plan2, H2, N2, d2, C2)
+
+    ref = _outputs(lib, plan, H, N, d, C)
+    plan.reassign(K, V, mu, out=ref, noalloc=True)
+    torch.cuda.synchronize()
+    out = _outputs(lib, plan, H, N, d, C)
+    eager = _outputs(lib, plan, H, N, d, C)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.reassign(K, V, mu, out=out, stream=side, noalloc=True)
+    side.synchronize()
+    say("[case] no-alloc reassign captured in a HIP graph")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        plan.reassign(K, V, mu, out=out, stream=side, noalloc=True)
+    torch.cuda.synchronize()
+    for r in range(3):
+        plan2.reassign(K2, V2, mu2, out=out2, noalloc=True)   # rewrites the shared scratch
+        plan.reassign(K, V, mu, out=eager)
+        for v in out.values():
+            v.fill_(-3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            x, y, z = ref[k], out[k], eager[k]
+            if x.dtype == torch.bfloat16:
+                x, y, z = x.view(torch.int16), y.view(torch.int16), z.view(torch.int16)
+            assert torch.equal(x, y), f"replay {r}: {k} differs from the eager call"
+            assert torch.equal(x, z), f"replay {r}: {k} differs between the entry points"
+    del graph
+    plan2.close()
+    plan.close()
 
 
 def test_noalloc_rejects_a_workspace_beyond_the_scratch(lib):
