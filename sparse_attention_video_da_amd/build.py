@@ -2,7 +2,8 @@
 
 Compiles the attention sources under csrc/ for gfx950 with hipcc and links one shared library
 exporting only the C ABI declared in include/decoupattn.h; the benchmark's peak probe
-(csrc/peak_probe.hip) becomes lib/libdapeak.so.
+(csrc/peak_probe.hip) becomes lib/libdapeak.so, and the plain-C example that a GPU test runs
+(tests/native/c_abi_example.c) becomes lib/c_abi_example, linked against the library.
 
     python sparse_attention_video_da_amd/build.py [--jobs N]
 """
@@ -23,6 +24,8 @@ LIB = os.path.join(LIBDIR, "libdecoupattn.so")
 SOURCES = ["api.cpp", "plan_lists.cpp", "forward.hip", "reassign.hip"]
 PEAK_SOURCE = "peak_probe.hip"
 PEAK_LIB = os.path.join(LIBDIR, "libdapeak.so")
+C_EXAMPLE_SOURCE = os.path.join(ROOT, "tests", "native", "c_abi_example.c")
+C_EXAMPLE = os.path.join(LIBDIR, "c_abi_example")
 ARCH = "gfx950"
 
 COMMON = [
@@ -74,7 +77,25 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     tmp = PEAK_LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe])
     os.replace(tmp, PEAK_LIB)
+    build_c_example()
     return LIB
+
+
+def build_c_example() -> str:
+    """The C ABI from plain C: compile tests/native/c_abi_example.c with the system C compiler
+    against lib/libdecoupattn.so (found next to the binary at run time)."""
+    cc = next((c for c in (os.environ.get("CC"), shutil.which("cc"), shutil.which("gcc")) if c),
+              None)
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C ABI example")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_EXAMPLE + ".tmp"
+    _run([cc, "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+          f"-I{os.path.join(ROOT, 'include')}", C_EXAMPLE_SOURCE, "-o", tmp, f"-L{LIBDIR}",
+          "-ldecoupattn", f"-L{rocm}/lib", "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN",
+          f"-Wl,-rpath,{rocm}/lib"])
+    os.replace(tmp, C_EXAMPLE)
+    return C_EXAMPLE
 
 
 def main(argv=None):
