@@ -3,13 +3,20 @@
 // counts n[b][c] (keys of cluster c outside query block b's exact key blocks).
 //
 // Kernel sequence per call (one stream, no host synchronisation):
-//   0. operands      (bf16) per centroid: -2 mu and the split |mu|^2 row for the MFMA.
+//   0. operands      (bf16) per centroid: -2 mu and the split |mu|^2 row for the MFMA;
+//                    clears the per-head near-tie counters.
 //   1. assign        MFMA distance product against centroid operands in LDS (bf16: the
 //                    whole table of a head resident when it fits in 128 KB, with a
-//                    persistent grid; streamed in chunks otherwise), per-lane running
-//                    argmin, written as int32 (bf16: any centroid within the 1e-4 relative
-//                    tie band of the nearest; fp32: lowest index on ties).
-//   2. block_hist    per key block, an LDS-atomic histogram of its keys' clusters.
+//                    persistent grid; streamed in chunks otherwise), per-lane running top
+//                    two, the nearest written as int32; keys whose top two are too close for
+//                    the expanded-form arithmetic go to a per-head near-tie list (fp32:
+//                    difference form, lowest index on ties). The resident form also writes
+//                    each key block's cluster histogram.
+//   1b. near ties    (bf16) the listed keys re-measured in difference form against every
+//                    centroid that could be their nearest; lowest index on equal distances;
+//                    a moved key's histogram counters are patched.
+//   2. block_hist    (streamed and fp32 assignments) per key block, an LDS-atomic
+//                    histogram of its keys' clusters.
 //   3. col_scan      per cluster, exclusive prefix of the histograms over key blocks
 //                    (where each block's keys start inside the cluster) and the sizes.
 //   4. starts        per head, exclusive prefix of the sizes over clusters.
