@@ -1,6 +1,6 @@
 """da_reassign_noalloc (the static-scratch variant of da_reassign) against da_reassign through the
-C ABI: two calls in a row on the same device, the second with a smaller layer (other H, N, d,
-C), replays of a captured HIP graph with other calls rewriting the scratch between them, and a
+C ABI: calls in a row on the same device, each followed by a smaller layer (other H, N, d, C;
+resident and streamed centroid tables), replays of a captured HIP graph with other calls rewriting the scratch between them, and a
 plan whose workspace exceeds the static scratch rejected before anything runs. The two entry
 points share their kernels, so every output must be identical bit for bit."""
 import ctypes
@@ -46,7 +46,10 @@ def _outputs(lib, plan, H, N, d, C):
 @pytest.mark.parametrize("order", ["noalloc_first", "plan_first"])
 def test_noalloc_matches_reassign_on_two_calls(lib, order):
     torch = torch_mod()
-    cases = [(4, 9000, 128, 128, 512, 7), (2, 2500, 64, 64, 100, 8)]   # second is smaller
+    # resident table, then a smaller layer; then a streamed table (C beyond the LDS-resident
+    # limit) and a smaller one again
+    cases = [(4, 9000, 128, 128, 512, 7), (2, 2500, 64, 64, 100, 8),
+             (2, 6000, 128, 128, 1536, 9), (1, 1800, 128, 64, 40, 10)]
     for i, (H, N, d, B, C, seed) in enumerate(cases):
         Kb, Vb, cache = _layer(seed, H, N, d, C, G=C // 2)
         nb = -(-N // B)
